@@ -1,0 +1,141 @@
+"""Pins for the acceptance interval (``oracle.check``).
+
+* the mechanics of TensorFold pull request #1123's range-checker bullet: value order with
+  -0 below +0, a one-value interval demands the same bits, NaN matches only NaN,
+  infinities compare by bits;
+* discrimination, after the page's planted controls ("Receipt", kernel-contract bullet): a
+  float32 emulation of chunked decode with an ordered merge passes the strict tier, while
+  the same emulation with one planted mistake (window one key early, merge without
+  exp(m_c - M), merge rounding toward zero, P rounded to one bf16 under the p32 interval)
+  fails it. The emulation is CPU test code built from numpy float32 steps.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attend, bf16, check
+from sliding_window_gqa_amd import workloads
+
+
+def b(x):
+    return bf16.to_bf16_bits(np.array(x, dtype=np.float64))
+
+
+def test_signed_zero_order():
+    # x = 0 with S = 0: the interval is the single value +0; -0 is outside it
+    assert check.accept(b([0.0]), [0.0], [0.0], 0.0).all()
+    assert not check.accept(b([-0.0]), [0.0], [0.0], 0.0).any()
+    # a tiny negative value rounds to -0; +0 lies above it
+    assert check.accept(b([-0.0]), [-1e-45], [0.0], 0.0).all()
+    assert not check.accept(b([0.0]), [-1e-45], [0.0], 0.0).any()
+    # an interval straddling zero holds both zeros
+    assert check.accept(b([-0.0, 0.0]), [1e-45, 1e-45], [1.0, 1.0], 0.0).all()
+
+
+def test_one_value_interval_is_bit_exact():
+    x = np.array([1.0 + 2.0 ** -10])            # well inside one bf16 cell, S tiny
+    assert check.accept(b([1.0]), x, [2.0 ** -30], 0.0, "S").all()
+    nxt = np.array([0x3F81], np.uint16)
+    assert not check.accept(nxt, x, [2.0 ** -30], 0.0, "S").any()
+    # tier G adds one ulp of relative width: the neighbour is accepted there
+    assert check.accept(nxt, x, [2.0 ** -30], 0.0, "G").all()
+
+
+def test_nan_and_infinities():
+    nan = np.array([0x7FC0], np.uint16)
+    assert check.accept(nan, [np.nan], [np.nan], 0.0).all()
+    assert not check.accept(b([1.0]), [np.nan], [np.nan], 0.0).any()
+    assert not check.accept(nan, [1.0], [1.0], 0.0).any()
+    assert check.accept(b([np.inf]), [np.inf], [np.inf], 0.0).all()
+    assert not check.accept(b([-np.inf]), [np.inf], [np.inf], 0.0).any()
+    assert not check.accept(b([3.0e38]), [np.inf], [np.inf], 0.0).any()
+
+
+def test_literal_stats_counts():
+    x = np.array([1.0, 1.0, 1.0, 2.0])
+    out = np.array([0x3F80, 0x3F81, 0x3F82, 0x4000], np.uint16)
+    st = check.literal_stats(out, x)
+    assert st == {"n": 4, "equal": 2, "within_1ulp": 3}
+
+
+# ---- float32 emulation of chunked decode (CPU test code, numpy float32 steps) -----------
+
+def emulate_decode(q, kc, vc, stream, pos, win, ring, chunk=256, early=0, no_rescale=False,
+                   truncate=False):
+    """Decode partials per absolute chunk, then an ordered merge, in float32."""
+    R, Hq, d = q.shape
+    G = Hq // kc.shape[2]
+    out = np.empty((R, Hq, d), np.uint16)
+    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    for r in range(R):
+        lo, last = attend.key_window(pos[r], win)
+        lo = max(0, lo - early)
+        for h in range(Hq):
+            ms, ls, os_ = [], [], []
+            for c in range(lo // chunk, last // chunk + 1):
+                keys = np.arange(max(lo, c * chunk), min(last, c * chunk + chunk - 1) + 1)
+                K = f(kc[stream[r], keys % ring, h // G])
+                V = f(vc[stream[r], keys % ring, h // G])
+                s = (K @ f(q[r, h])).astype(np.float32)
+                m = s.max()
+                p = np.exp(s - m).astype(np.float32)
+                ms.append(m); ls.append(p.sum(dtype=np.float32)); os_.append((p @ V).astype(np.float32))
+            M = max(ms)
+            num = np.zeros(d, np.float32)
+            den = np.float32(0)
+            for m, l, o in zip(ms, ls, os_):
+                a = np.float32(1) if no_rescale else np.exp(np.float32(m - M))
+                num = (num + a * o).astype(np.float32)
+                den = np.float32(den + a * l)
+            y = (num / den).astype(np.float32)
+            out[r, h] = (y.view(np.uint32) >> 16).astype(np.uint16) if truncate else \
+                workloads._bf16_bits(y)
+    return out
+
+
+@pytest.fixture(scope="module")
+def small_decode():
+    return workloads.decode_case("checker discrimination", 6, 4, 2, 256, 300, 700, 2,
+                                 [299, 512, 690, 1000, 1400, 255], seed=11, peak_every=2)
+
+
+def _strict_fails(case, out):
+    x, S, _ = attend.decode(case.q, case.k, case.v, case.stream, case.pos, case.win, case.ring, 1.0)
+    return int((~check.accept(out, x, S, check.E_P_FP32, "S")).sum())
+
+
+def test_fp32_emulation_passes_strict(small_decode):
+    c = small_decode
+    out = emulate_decode(c.q, c.k, c.v, c.stream, c.pos, c.win, c.ring)
+    assert _strict_fails(c, out) == 0
+
+
+@pytest.mark.parametrize("kw", [{"early": 1}, {"no_rescale": True}, {"truncate": True}])
+def test_planted_mistakes_go_red(small_decode, kw):
+    c = small_decode
+    out = emulate_decode(c.q, c.k, c.v, c.stream, c.pos, c.win, c.ring, **kw)
+    assert _strict_fails(c, out) > 0
+
+
+def test_one_bf16_p_goes_red_under_the_p32_interval():
+    case = workloads.prompt_case("p32 control", 24, 2, 1, 256, 40, 64, 128, seed=12)
+    x, S, _ = attend.prompt(case.q, case.k, case.v, case.p0, case.win, case.ring, 1.0)
+    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    outs = {}
+    for mode in ("p32", "bf16"):
+        out = np.empty_like(case.q)
+        for i in range(case.n):
+            lo, last = attend.key_window(case.p0 + i, case.win)
+            keys = np.arange(lo, last + 1) % case.ring
+            for h in range(case.hq):
+                K, V = f(case.k[keys, 0]), f(case.v[keys, 0])
+                s = (K @ f(case.q[i, h])).astype(np.float32)
+                p = np.exp(s - s.max()).astype(np.float32)
+                hi = f(workloads._bf16_bits(p))
+                lo_ = f(workloads._bf16_bits(p - hi))
+                pp = hi + lo_ if mode == "p32" else hi
+                y = ((pp @ V) / p.sum(dtype=np.float32)).astype(np.float32)
+                out[i, h] = workloads._bf16_bits(y)
+        outs[mode] = int((~check.accept(out, x, S, check.E_P_P32, "S")).sum())
+    assert outs["p32"] == 0
+    assert outs["bf16"] > 0
