@@ -1,0 +1,292 @@
+"""Throughput of windowed GQA attention on one MI355X: decode KV GB/s and prefill TFLOP/s.
+
+One step is one pass of the whole hot path of a Gemma-4-12B-shaped sliding layer:
+  * decode: 64 rows over 3 streams, 16/8 heads x 256, window 1024 over a ring of 1536,
+    positions up to 40,000 (split-KV chunk partials + ordered merge), and
+  * prompt: a 512-row chunk at p0 5,000 with p32 and an image span (MFMA online softmax).
+``value`` is the decode's key/value bytes per second in the accounting of TensorFold pull
+request #1123's receipt (each row reads its visible keys' K and V: 8 MiB for a full 12B
+row), with caches flushed from L2/MALL before every timed decode call. Prefill throughput
+is reported beside it, and the long non-windowed prompt (37,810 x 56 x 128, non-causal) is
+timed on its own as the MFMA-bound shape.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--long-iters 3] [--no-cpu]
+
+Prints one JSON line.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sliding_window_gqa_amd import api, workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 256
+
+
+def key_span(pos, win, last=None):
+    lo = max(0, pos - win + 1) if win > 0 else 0
+    return lo, pos if last is None else last
+
+
+def decode_units(case):
+    """Per the receipt's accounting: K and V bytes of every visible key of every row, plus q
+    and out; and the unique K/V bytes (distinct ring slots touched per stream and head)."""
+    per_row = 0
+    slots = {}
+    for r in range(case.rows):
+        lo, last = key_span(int(case.pos[r]), case.win)
+        per_row += (last - lo + 1) * case.hkv * case.d * 2 * 2
+        s = slots.setdefault(int(case.stream[r]), np.zeros(case.ring, bool))
+        s[np.arange(lo, last + 1) % case.ring] = True
+    unique = sum(int(s.sum()) for s in slots.values()) * case.hkv * case.d * 2 * 2
+    qo = 2 * case.rows * case.hq * case.d * 2
+    flops = 0
+    G = case.hq // case.hkv
+    for r in range(case.rows):
+        lo, last = key_span(int(case.pos[r]), case.win)
+        flops += (last - lo + 1) * case.hkv * G * case.d * 2 * 2
+    return {"kv_bytes": per_row, "unique_bytes": unique + qo, "row_bytes": per_row + qo,
+            "flops_fp32": flops}
+
+
+def prompt_units(case):
+    """MFMA flops the method performs: 2d for S and 2d per P.V product per visible
+    (row, head, key); p32 runs P.V twice."""
+    pv = 2 if case.p32 else 1
+    triples = 0
+    for i in range(case.n):
+        last = None if case.hi is None else int(case.hi[i])
+        lo, hi = key_span(case.p0 + i, case.win, last)
+        triples += (hi - lo + 1)
+    triples *= case.hq
+    flops = triples * (2 + 2 * pv) * case.d
+    byts = (case.q.size + case.q.size + 2 * case.k.shape[0] * case.k.shape[1] * case.d) * 2
+    return {"triples": triples, "flops": flops, "bytes": byts}
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Timed:
+    """HIP events on the current stream around each call."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def ms(self):
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+class Decoder:
+    """Decode inputs resident on the device and the C-ABI call prepared once (so the timed
+    region holds no Python marshalling)."""
+
+    def __init__(self, case):
+        self.c = case
+        self.q = to_dev(case.q)
+        self.k = to_dev(case.k)
+        self.v = to_dev(case.v)
+        self.st = torch.from_numpy(case.stream.astype(np.int32)).cuda()
+        self.pos = torch.from_numpy(case.pos.astype(np.int32)).cuda()
+        n = api.decode_workspace_bytes(case.rows, case.hq, case.d, case.win, case.ring, api.INT32_MAX)
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((case.rows, case.hq, case.d), dtype=torch.bfloat16, device="cuda")
+        # one checked call through the binding, then the raw call with the same arguments
+        api.decode(self.q, self.k, self.v, self.st, self.pos, case.win, case.ring, case.scale,
+                   out=self.out, workspace=self.ws)
+        self.w = api.window(case.win, case.ring, case.scale)
+        k = self.k
+        self.args = (ctypes.byref(self.w), self.q.data_ptr(), self.q.stride(0), self.q.stride(1),
+                     k.data_ptr(), self.v.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+                     k.shape[0], self.st.data_ptr(), self.pos.data_ptr(), api.INT32_MAX,
+                     case.rows, case.hq, case.hkv, case.d, self.ws.data_ptr(), self.ws.numel(),
+                     self.out.data_ptr(), self.out.stride(0), self.out.stride(1),
+                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self.fn = api.lib().wa_decode
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"wa_decode status {st}")
+
+
+class Prompter:
+    def __init__(self, case):
+        self.c = case
+        if case.buffer is not None:
+            buf = to_dev(case.buffer)
+            n, heads, d = case.q.shape
+            hd = heads * d
+            self.q = buf[:, 0:hd].view(n, heads, d)
+            self.k = buf[:, hd:2 * hd].view(n, heads, d)
+            self.v = buf[:, 2 * hd:3 * hd].view(n, heads, d)
+        else:
+            self.q, self.k, self.v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+        self.hi = None if case.hi is None else torch.from_numpy(case.hi.astype(np.int32)).cuda()
+        self.out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
+        api.prompt(self.q, self.k, self.v, case.p0, case.win, case.ring, case.scale, hi=self.hi,
+                   p32=case.p32, out=self.out)
+        self.w = api.window(case.win, case.ring, case.scale, case.p32)
+        q, k = self.q, self.k
+        self.args = (ctypes.byref(self.w), q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(),
+                     self.v.data_ptr(), k.stride(0), k.stride(1), case.p0, case.n, case.hq,
+                     case.hkv, case.d, None if self.hi is None else self.hi.data_ptr(),
+                     self.out.data_ptr(), self.out.stride(0), self.out.stride(1),
+                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self.fn = api.lib().wa_prompt
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"wa_prompt status {st}")
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The float64 oracle on the decode workload's rows, on the host cores."""
+    from oracle import attend
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    units = decode_units(case)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        attend.decode(case.q, case.k, case.v, case.stream, case.pos, case.win, case.ring, case.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(units["kv_bytes"] * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"all {case.rows} rows of the decode workload, {reps} pass(es) in {dt:.1f} s "
+                      f"(numpy float64, BLAS threads as shown)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--long-iters", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards without exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    api.lib()
+
+    dcase = workloads.decode_12b()
+    pcase = workloads.prompt_12b()
+    dec, pro = Decoder(dcase), Prompter(pcase)
+    du, pu = decode_units(dcase), prompt_units(pcase)
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")  # > MALL (256 MB)
+
+    for _ in range(args.warmup):
+        dec(); pro()
+    torch.cuda.synchronize()
+    td, tp = Timed(), Timed()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        flush.fill_(1)
+        with td:
+            dec()
+        with tp:
+            pro()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dms = float(np.mean(td.ms()))
+    pms = float(np.mean(tp.ms()))
+    # warm-cache decode, for reference
+    tw = Timed()
+    for _ in range(args.steps):
+        with tw:
+            dec()
+    dms_warm = float(np.mean(tw.ms()))
+
+    kv_gbs = du["kv_bytes"] / (dms * 1e-3) / 1e9
+    pre_tfs = pu["flops"] / (pms * 1e-3) / 1e12
+    res = {
+        "metric": "decode KV GB/s + prefill TFLOP/s, hd256 GQA window attn, % of roofline",
+        "value": round(kv_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dms + pms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded; receipt distributions)",
+        "config": {"workload": "Gemma-4-12B-shaped sliding layer step: decode 64 rows over 3 "
+                               "streams (16/8 x 256, window 1024, ring 1536, pos < 40,000) + "
+                               "prompt chunk 512 rows at p0 5,000 (p32, image rows 40..300)",
+                   "decode_rows": 64, "prompt_rows": 512, "window": 1024, "ring": 1536},
+        "decode": {"ms": round(dms, 5), "ms_warm_cache": round(dms_warm, 5),
+                   "kv_bytes_per_call": du["kv_bytes"], "unique_bytes_per_call": du["unique_bytes"],
+                   "kv_gbs_warm": round(du["kv_bytes"] / (dms_warm * 1e-3) / 1e9, 2),
+                   "unique_gbs": round(du["unique_bytes"] / (dms * 1e-3) / 1e9, 2)},
+        "prefill": {"ms": round(pms, 5), "tflops": round(pre_tfs, 2), "flops_per_call": pu["flops"],
+                    "flop_accounting": "(2 + 2*2) * d per visible (row, head, key), p32"},
+        "wall_s_timed_loop": round(wall, 3),
+    }
+    rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s")
+    rl_decode = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
+    rl_prompt["kernel"] = "prompt_kernel<256,p32> (12B prompt chunk)"
+    rl_decode["kernel"] = "decode_part_kernel<256,2> + merge_kernel<256> (unique K/V bytes)"
+    res["roofline"] = rl_prompt if pms >= dms else rl_decode
+    res["roofline_decode"] = rl_decode
+
+    if not args.no_long:
+        lcase = workloads.long_prompt()
+        lp = Prompter(lcase)
+        lu = prompt_units(lcase)
+        lp(); torch.cuda.synchronize()
+        tl = Timed()
+        for _ in range(args.long_iters):
+            with tl:
+                lp()
+        lms = float(np.mean(tl.ms()))
+        ltf = lu["flops"] / (lms * 1e-3) / 1e12
+        res["prefill_long"] = {"workload": "long non-windowed prompt 37,810 x 56 x 128, non-causal, bf16 P",
+                               "ms": round(lms, 3), "tflops": round(ltf, 2),
+                               "flops_per_call": lu["flops"]}
+        rl = roofline("mfma", ltf, MFMA_BF16_PEAK_TFS, "TFLOP/s")
+        rl["kernel"] = "prompt_kernel<128,bf16P> (long prompt)"
+        res["roofline_prefill_long"] = rl
+        del lp
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(dcase)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * wa.h -- windowed grouped-query softmax attention on MI355X (gfx950), C ABI.
+ *
+ * The operation (TensorFold pull request #1123, "window_attention at head dim 256",
+ * section "What this changes"): for each query row i at key position p_i and each query
+ * head h, with key head g = h / G (G = hq / hkv query heads per key head, any G up to 16),
+ *
+ *     visible keys   j in [lo_i, last_i],  lo_i = max(0, p_i - window + 1)  (0 if window == 0)
+ *     score          s_j  = scale * (q_i,h . k_j,g)
+ *     output         o_i,h = sum_j softmax(s)_j v_j,g, rounded once to bf16 (nearest-even)
+ *
+ * last_i is the row's own position, or hi[i] in the prompt form ("promptRows(..., hi)"
+ * bullet). Key j is stored in ring slot j mod ring ("Scale/Window 0" bullet; window 0
+ * means a linear cache, i.e. a ring as long as the cache).
+ *
+ * Two forms:
+ *   decode  split-KV over 256-key chunks at absolute key positions, per-chunk partials
+ *           (m_c, l_c, o_c) in fp32 with fp32 probabilities, then a merge over the chunks in
+ *           chunk order ("Decode" bullet). A row's bits do not depend on the batch, the
+ *           stream slot or the declared cache length.
+ *   prompt  rows p0 .. p0+n-1 of one stream, tiled online softmax on MFMA (bf16 products,
+ *           fp32 accumulation), key tiles at absolute positions ("Prompt" bullet); P enters
+ *           P.V as one bf16, or with p32 as bf16(P) + bf16(P - bf16(P)) ("Window.p32" bullet).
+ *           A row's bits do not depend on how the prompt is chunked.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; every tensor pointer is a DEVICE
+ *     pointer; strides are in elements; the innermost (dim) stride is 1.
+ *   - q/out are [rows][hq][d] with row and head strides; the K and V caches share one layout
+ *     [stream][slot][kv head][d] with stream, slot and head strides.
+ *   - d is 128 or 256; hq % hkv == 0 and hq / hkv <= 16.
+ *   - The library allocates, frees and synchronises nothing, and keeps no per-call state; it
+ *     is safe to call from several host threads. Work is queued on `stream` (a hipStream_t;
+ *     NULL is the default stream). Inputs must stay alive and unchanged, and outputs must not
+ *     be read, until that stream has completed the call.
+ *   - Host-checkable mistakes return a negative status and launch nothing. Device-side
+ *     preconditions (positions, stream indices, hi) cannot be checked without a
+ *     synchronisation; the kernels clamp them into range so that every access stays inside
+ *     the caller's buffers, and the result for a violating row is then unspecified.
+ *   - Until the float64 re-run of non-finite rows exists, a non-finite output has the class
+ *     that fp32 arithmetic gives. That is float64's class except where a weight that float64
+ *     keeps underflows to zero in fp32 beside an infinite value (0 * inf), or where finite
+ *     inputs overflow fp32 in q . k.
+ */
+#ifndef WA_H
+#define WA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Window parameters shared by both forms ("Window" in the pull request). */
+typedef struct wa_window {
+    int32_t window;  /* keys a row sees up to its last key; 0 = no window (linear cache) */
+    int32_t ring;    /* slots per stream in the K/V cache (the cache length when window == 0) */
+    float   scale;   /* score scale: s = scale * (q . k) */
+    int32_t p32;     /* prompt only: nonzero = P as two bf16 halves, zero = P as one bf16 */
+} wa_window_t;
+
+enum {
+    WA_OK = 0,
+    WA_EARG = -1,          /* null pointer, non-positive size, bad stride */
+    WA_EUNSUPPORTED = -2,  /* head dim other than 128/256, hq % hkv != 0, group > 16 */
+    WA_ERANGE = -3,        /* window/ring inconsistent with the positions the call can reach */
+    WA_EWORKSPACE = -4,    /* decode workspace missing or smaller than wa_decode_workspace() */
+    WA_EHIP = -5           /* a kernel launch failed (hipGetLastError after the launch) */
+};
+
+/* Most chunks a decode row can span: window > 0: (window - 1 + 255) / 256 + 1;
+ * window == 0: max_pos / 256 + 1. Returns 0 for invalid arguments. */
+int32_t wa_decode_chunks(const wa_window_t* w, int32_t max_pos);
+
+/* Bytes of device workspace wa_decode needs for `rows` rows of `hq` heads of dim `d`:
+ * fp32 partials m, l [rows][hq][C] and o [rows][hq][C][d], C = wa_decode_chunks(). 0 on error. */
+size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_t* w,
+                           int32_t max_pos);
+
+/*
+ * Decode: row r (0 <= r < rows) of stream stream_of_row[r] at position pos_of_row[r] (both
+ * device int32 arrays) attends over keys [lo_r, pos_r] of its stream's ring. Launches the
+ * chunk-partial kernel (one workgroup per (row, key head, chunk)) and the ordered merge.
+ *   q        [rows][hq][d]          strides q_srow, q_shead
+ *   k, v     [streams][ring][hkv][d] strides kv_sstream, kv_sslot, kv_shead
+ *   max_pos  an upper bound of every pos_of_row[r] (sizes the chunk grid when window == 0)
+ *   ws       device workspace of ws_bytes >= wa_decode_workspace(rows, hq, d, w, max_pos)
+ *   out      [rows][hq][d]          strides o_srow, o_shead
+ * Device preconditions: 0 <= pos_of_row[r] <= max_pos, 0 <= stream_of_row[r] < streams, and
+ * the ring holds keys [lo_r, pos_r] of row r's stream in slots j mod ring. Errors: WA_EARG,
+ * WA_EUNSUPPORTED, WA_ERANGE (window > ring, or window == 0 and max_pos >= ring),
+ * WA_EWORKSPACE, WA_EHIP.
+ */
+int wa_decode(const wa_window_t* w,
+              const uint16_t* q, int64_t q_srow, int64_t q_shead,
+              const uint16_t* k, const uint16_t* v,
+              int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+              const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+              int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+              void* ws, size_t ws_bytes,
+              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
+
+/*
+ * Merge of decode partials (the second half of wa_decode, exposed so that partials made
+ * elsewhere, e.g. gathered from several devices, can be combined with the same bits).
+ * For row r and head h it reads chunks c = 0 .. n_r - 1 of the partial arrays, where n_r is
+ * the number of 256-key chunks holding keys [lo_r, pos_r] (pos from pos_of_row), in chunk
+ * order: M = max m_c, a_c = exp(m_c - M), out = bf16(sum a_c o_c / sum a_c l_c), both sums
+ * fma chains over the chunks in order ("Decode" bullet of the pull request).
+ *   m, l  [rows][hq][C] fp32      o  [rows][hq][C][d] fp32       C = chunk capacity
+ * Device precondition: n_r <= C (rows violating it read only their first C chunks).
+ * Errors: WA_EARG, WA_EUNSUPPORTED, WA_EHIP.
+ */
+int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* o,
+             const int32_t* pos_of_row, int32_t rows, int32_t hq, int32_t C, int32_t d,
+             uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
+
+/*
+ * Prompt: rows i = 0 .. n-1 at positions p0 + i of one stream. Row i sees keys
+ * [lo_i, last_i] with last_i = hi[i] if hi is not NULL (device int32 [n],
+ * p0 + i <= hi[i] < p0 + n), else p0 + i.
+ *   q        [n][hq][d]       strides q_srow, q_shead
+ *   k, v     [ring][hkv][d]   strides kv_sslot, kv_shead (one stream's ring)
+ *   out      [n][hq][d]       strides o_srow, o_shead
+ * The ring must hold keys [min lo_i, p0 + n - 1] without two of them sharing a slot:
+ * ring >= p0 + n - max(0, p0 - window + 1) (window > 0) or ring >= p0 + n (window == 0),
+ * else WA_ERANGE. hi values out of range are clamped into [p0 + i, p0 + n - 1].
+ * Errors: WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EHIP.
+ */
+int wa_prompt(const wa_window_t* w,
+              const uint16_t* q, int64_t q_srow, int64_t q_shead,
+              const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
+              int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
+              const int32_t* hi,
+              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* wa_status_string(int status);
+
+/* Library version string (static storage). */
+const char* wa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WA_H */

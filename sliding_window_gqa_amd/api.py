@@ -1,0 +1,159 @@
+"""Thin ctypes binding of ``libwa.so`` (C ABI in include/wa.h).
+
+Argument marshalling only: tensors supply device pointers and strides, torch's current
+stream supplies the HIP stream, and every step of the computation runs in the library's
+HIP kernels. There is no fallback: if ``libwa.so`` is missing or a GPU is absent, the
+calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwa.so")
+INT32_MAX = 2**31 - 1
+
+_lib = None
+
+
+class Window(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("ring", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("p32", ctypes.c_int32)]
+
+
+def window(window, ring, scale=1.0, p32=False):
+    return Window(int(window), int(ring), float(scale), 1 if p32 else 0)
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_WP = ctypes.POINTER(Window)
+
+SIGNATURES = {
+    "wa_decode_chunks": (_I32, [_WP, _I32]),
+    "wa_decode_workspace": (_SZ, [_I32, _I32, _I32, _WP, _I32]),
+    "wa_decode": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I32,
+                                 _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ,
+                                 _P, _I64, _I64, _P]),
+    "wa_merge": (ctypes.c_int, [_WP, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                _P, _I64, _I64, _P]),
+    "wa_prompt": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64,
+                                 _I32, _I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P]),
+    "wa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "wa_version": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load libwa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sliding_window_gqa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise RuntimeError(f"wa: {lib().wa_status_string(status).decode()} (status {status})")
+
+
+def _bf16(t, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the innermost (dim) stride must be 1")
+    return t
+
+
+def _i32(t, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 CUDA tensor")
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def decode_workspace_bytes(rows, hq, d, win, ring, max_pos):
+    w = window(win, ring)
+    return lib().wa_decode_workspace(rows, hq, d, ctypes.byref(w), max_pos)
+
+
+def decode(q, k, v, stream_of_row, pos_of_row, win, ring, scale=1.0, max_pos=None,
+           out=None, workspace=None):
+    """Decode rows. q [rows, Hq, d]; k, v [streams, ring, Hkv, d] (bf16, CUDA);
+    stream_of_row, pos_of_row int32 [rows] (CUDA). Returns out [rows, Hq, d] bf16."""
+    _bf16(q, "q"); _bf16(k, "k"); _bf16(v, "v")
+    _i32(stream_of_row, "stream_of_row"); _i32(pos_of_row, "pos_of_row")
+    if k.shape != v.shape or k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must share one [streams, ring, Hkv, d] layout")
+    rows, hq, d = q.shape
+    streams, ring_k, hkv, dk = k.shape
+    if dk != d or ring_k != ring:
+        raise ValueError("k/v shape does not match q or the ring length")
+    if max_pos is None:
+        max_pos = INT32_MAX if win > 0 else ring - 1
+    w = window(win, ring, scale)
+    need = lib().wa_decode_workspace(rows, hq, d, ctypes.byref(w), max_pos)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((rows, hq, d), dtype=torch.bfloat16, device=q.device)
+    _check(lib().wa_decode(ctypes.byref(w), q.data_ptr(), q.stride(0), q.stride(1),
+                           k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+                           streams, stream_of_row.data_ptr(), pos_of_row.data_ptr(), max_pos,
+                           rows, hq, hkv, d, workspace.data_ptr(), workspace.numel(),
+                           out.data_ptr(), out.stride(0), out.stride(1), _stream()))
+    return out
+
+
+def merge(m, l, o, pos_of_row, win, ring, out=None):
+    """Merge decode partials m, l [rows, Hq, C] and o [rows, Hq, C, d] (fp32, CUDA)."""
+    for t, nm in ((m, "m"), (l, "l"), (o, "o")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous float32 CUDA tensor")
+    _i32(pos_of_row, "pos_of_row")
+    rows, hq, C, d = o.shape
+    if out is None:
+        out = torch.empty((rows, hq, d), dtype=torch.bfloat16, device=o.device)
+    w = window(win, ring)
+    _check(lib().wa_merge(ctypes.byref(w), m.data_ptr(), l.data_ptr(), o.data_ptr(),
+                          pos_of_row.data_ptr(), rows, hq, C, d, out.data_ptr(),
+                          out.stride(0), out.stride(1), _stream()))
+    return out
+
+
+def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None):
+    """Prompt rows p0 .. p0+n-1. q [n, Hq, d]; k, v [ring, Hkv, d] (bf16, CUDA, any
+    strides with a unit dim stride); hi int32 [n] (CUDA) or None."""
+    _bf16(q, "q"); _bf16(k, "k"); _bf16(v, "v")
+    if k.shape != v.shape or k.stride() != v.stride() or k.dim() != 3:
+        raise ValueError("k and v must share one [ring, Hkv, d] layout")
+    n, hq, d = q.shape
+    ring_k, hkv, dk = k.shape
+    if dk != d or ring_k < ring:
+        raise ValueError("k/v shape does not match q or the ring length")
+    hp = None
+    if hi is not None:
+        _i32(hi, "hi")
+        hp = hi.data_ptr()
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.bfloat16, device=q.device)
+    w = window(win, ring, scale, p32)
+    _check(lib().wa_prompt(ctypes.byref(w), q.data_ptr(), q.stride(0), q.stride(1),
+                           k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
+                           int(p0), n, hq, hkv, d, hp, out.data_ptr(), out.stride(0),
+                           out.stride(1), _stream()))
+    return out

@@ -1,0 +1,142 @@
+// C ABI of the wa library: argument checks, workspace sizing and kernel dispatch.
+// The operation and the conventions are documented in include/wa.h.
+#include "wa_common.h"
+#include "../../include/wa.h"
+
+namespace {
+
+bool head_shape_ok(int32_t hq, int32_t hkv, int32_t d) {
+    if (d != 128 && d != 256) return false;
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+    return hq / hkv <= 16;
+}
+
+bool window_ok(const wa_window_t* w) {
+    return w && w->window >= 0 && w->ring > 0 && w->scale == w->scale;
+}
+
+int chunk_capacity(const wa_window_t* w, int32_t max_pos) {
+    if (!window_ok(w) || max_pos < 0) return 0;
+    if (w->window > 0) return (w->window - 1 + wa::kChunk - 1) / wa::kChunk + 1;
+    return max_pos / wa::kChunk + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wa_decode_chunks(const wa_window_t* w, int32_t max_pos) {
+    return chunk_capacity(w, max_pos);
+}
+
+size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_t* w,
+                           int32_t max_pos) {
+    const int C = chunk_capacity(w, max_pos);
+    if (C <= 0 || rows <= 0 || hq <= 0 || (d != 128 && d != 256)) return 0;
+    const size_t cells = (size_t)rows * (size_t)hq * (size_t)C;
+    return cells * sizeof(float) * (2 + (size_t)d);
+}
+
+int wa_decode(const wa_window_t* w,
+              const uint16_t* q, int64_t q_srow, int64_t q_shead,
+              const uint16_t* k, const uint16_t* v,
+              int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+              const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+              int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+              void* ws, size_t ws_bytes,
+              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    if (!w || !q || !k || !v || !stream_of_row || !pos_of_row || !out) return WA_EARG;
+    if (rows <= 0 || streams <= 0 || max_pos < 0) return WA_EARG;
+    if (q_srow < 0 || q_shead < 0 || kv_sstream < 0 || kv_sslot < 0 || kv_shead < 0 ||
+        o_srow < 0 || o_shead < 0)
+        return WA_EARG;
+    if (!head_shape_ok(hq, hkv, d)) return WA_EUNSUPPORTED;
+    if (!window_ok(w)) return WA_EARG;
+    if (w->window > w->ring) return WA_ERANGE;
+    if (w->window == 0 && max_pos >= w->ring) return WA_ERANGE;
+    const size_t need = wa_decode_workspace(rows, hq, d, w, max_pos);
+    if (!ws || ws_bytes < need || need == 0) return WA_EWORKSPACE;
+    // 16-byte vector loads of q and K/V rows
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
+    if ((q_srow | q_shead | kv_sstream | kv_sslot | kv_shead) & 7) return WA_EARG;
+
+    wa::DecodeArgs a{};
+    a.q = q; a.q_srow = q_srow; a.q_shead = q_shead;
+    a.k = k; a.v = v; a.kv_sstream = kv_sstream; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
+    a.streams = streams; a.stream_of_row = stream_of_row; a.pos_of_row = pos_of_row;
+    a.max_pos = max_pos; a.rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
+    a.window = w->window; a.ring = w->ring; a.scale = w->scale;
+    a.C = chunk_capacity(w, max_pos);
+    const size_t cells = (size_t)rows * hq * a.C;
+    a.m = static_cast<float*>(ws);
+    a.l = a.m + cells;
+    a.o = a.l + cells;
+    a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (wa::launch_decode_part(a, s) != hipSuccess) return WA_EHIP;
+    if (wa::launch_merge(a, s) != hipSuccess) return WA_EHIP;
+    return WA_OK;
+}
+
+int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* o,
+             const int32_t* pos_of_row, int32_t rows, int32_t hq, int32_t C, int32_t d,
+             uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    if (!w || !m || !l || !o || !pos_of_row || !out) return WA_EARG;
+    if (rows <= 0 || hq <= 0 || C <= 0 || o_srow < 0 || o_shead < 0) return WA_EARG;
+    if (d != 128 && d != 256) return WA_EUNSUPPORTED;
+    if (!window_ok(w)) return WA_EARG;
+    wa::DecodeArgs a{};
+    a.m = const_cast<float*>(m); a.l = const_cast<float*>(l); a.o = const_cast<float*>(o);
+    a.pos_of_row = pos_of_row; a.rows = rows; a.hq = hq; a.hkv = hq; a.d = d; a.C = C;
+    a.window = w->window; a.ring = w->ring; a.scale = w->scale;
+    a.max_pos = 0x7FFFFFFF;
+    a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    if (wa::launch_merge(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
+    return WA_OK;
+}
+
+int wa_prompt(const wa_window_t* w,
+              const uint16_t* q, int64_t q_srow, int64_t q_shead,
+              const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
+              int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
+              const int32_t* hi,
+              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    if (!w || !q || !k || !v || !out) return WA_EARG;
+    if (n <= 0 || p0 < 0) return WA_EARG;
+    if (q_srow < 0 || q_shead < 0 || kv_sslot < 0 || kv_shead < 0 || o_srow < 0 || o_shead < 0)
+        return WA_EARG;
+    if (!head_shape_ok(hq, hkv, d)) return WA_EUNSUPPORTED;
+    if (!window_ok(w)) return WA_EARG;
+    if ((int64_t)p0 + n > 0x7FFFFFFF) return WA_ERANGE;
+    const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
+    if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
+    if ((q_srow | q_shead | kv_sslot | kv_shead) & 7) return WA_EARG;
+    if (((uintptr_t)out & 7) || ((o_srow | o_shead) & 3)) return WA_EARG;
+
+    wa::PromptArgs a{};
+    a.q = q; a.q_srow = q_srow; a.q_shead = q_shead;
+    a.k = k; a.v = v; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
+    a.p0 = p0; a.n = n; a.hq = hq; a.hkv = hkv; a.d = d;
+    a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p32 = w->p32 != 0;
+    a.hi = hi;
+    a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    if (wa::launch_prompt(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
+    return WA_OK;
+}
+
+const char* wa_status_string(int status) {
+    switch (status) {
+        case WA_OK: return "ok";
+        case WA_EARG: return "invalid argument";
+        case WA_EUNSUPPORTED: return "unsupported shape";
+        case WA_ERANGE: return "window or ring inconsistent with the positions";
+        case WA_EWORKSPACE: return "workspace missing or too small";
+        case WA_EHIP: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* wa_version(void) { return "wa 0.1 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Shared device helpers and the launcher declarations for the wa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wa {
+
+constexpr int kChunk = 256;      // decode chunk: keys at absolute positions [256c, 256c + 255]
+
+// bf16 bits -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+// low / high bf16 of a packed pair -> fp32
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN, overflow goes to inf, an
+// underflow to zero keeps its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// Lane exchange across the whole wave (ds_bpermute).
+__device__ __forceinline__ float xor_shfl(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+struct DecodeArgs {
+    const uint16_t* q; int64_t q_srow, q_shead;
+    const uint16_t* k; const uint16_t* v;
+    int64_t kv_sstream, kv_sslot, kv_shead; int32_t streams;
+    const int32_t* stream_of_row; const int32_t* pos_of_row; int32_t max_pos;
+    int32_t rows, hq, hkv, d;
+    int32_t window, ring; float scale;
+    int32_t C;                    // chunk capacity of the partial arrays
+    float* m; float* l; float* o; // partials
+    uint16_t* out; int64_t o_srow, o_shead;
+};
+
+struct PromptArgs {
+    const uint16_t* q; int64_t q_srow, q_shead;
+    const uint16_t* k; const uint16_t* v; int64_t kv_sslot, kv_shead;
+    int32_t p0, n, hq, hkv, d;
+    int32_t window, ring; float scale; int32_t p32;
+    const int32_t* hi;
+    uint16_t* out; int64_t o_srow, o_shead;
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_decode_part(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
+
+}  // namespace wa

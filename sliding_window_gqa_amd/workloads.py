@@ -15,6 +15,7 @@ rounding float32 draws with torch's float32 -> bfloat16 conversion (round to nea
 and are handed out as uint16 bit patterns.
 """
 
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -209,19 +210,29 @@ def prompt_31b(seed=1004):
                        333, 32, 16, 256, 1300, 1024, 1536, seed)
 
 
-def long_prompt(seed=1005, n=37810, heads=56, d=128, p32=False, block=2048):
+def long_prompt(seed=1005, n=37810, heads=56, d=128, p32=False, block=1024):
     """Non-windowed, non-causal prompt over a linear cache: n tokens, ``heads`` heads of d,
     scale fl32(1/sqrt(d)). Q/K/V are N(0,1) draws normalised to unit RMS per (token, head)
     with eps 1e-5, in one interleaved [n, 3*heads*d] buffer (Q, K, V column blocks).
-    Every row's last key is n - 1."""
-    rng = np.random.Generator(np.random.PCG64(seed))
+    Every row's last key is n - 1. Token block b (``block`` tokens) draws from its own
+    PCG64 stream, spawned from ``seed``, so blocks can be generated in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
     width = 3 * heads * d
     buf = np.empty((n, width), dtype=np.uint16)
-    for a in range(0, n, block):
+    starts = list(range(0, n, block))
+    seqs = np.random.SeedSequence(seed).spawn(len(starts))
+
+    def fill(i):
+        a = starts[i]
         b = min(n, a + block)
+        rng = np.random.Generator(np.random.PCG64(seqs[i]))
         z = rng.standard_normal((b - a, 3 * heads, d), dtype=np.float32)
-        z = z / np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + np.float32(1e-5))
+        z /= np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + np.float32(1e-5))
         buf[a:b] = _bf16_bits(z).reshape(b - a, width)
+
+    workers = min(16, max(1, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(len(starts))))
     hd = heads * d
     q = buf[:, 0:hd].reshape(n, heads, d)
     k = buf[:, hd:2 * hd].reshape(n, heads, d)

@@ -1,0 +1,89 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, call the library
+through its binding, and compare with the float64 oracle."""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attend, check
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a):
+    """uint16 numpy array (any strides) -> bf16 CUDA tensor with the same element strides."""
+    a = np.asarray(a)
+    if a.base is not None and not a.flags.c_contiguous:
+        raise ValueError("use dev_view for strided views")
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_view(buf_dev, view, base_np):
+    """Strided bf16 CUDA view of ``buf_dev`` matching the numpy view ``view`` of ``base_np``."""
+    item = base_np.itemsize
+    off = (view.__array_interface__["data"][0] - base_np.__array_interface__["data"][0]) // item
+    return torch.as_strided(buf_dev, view.shape, [s // item for s in view.strides], off)
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_decode(case, **kw):
+    from sliding_window_gqa_amd import api
+    out = api.decode(dev_bf16(case.q), dev_bf16(case.k), dev_bf16(case.v), dev_i32(case.stream),
+                     dev_i32(case.pos), case.win, case.ring, case.scale, **kw)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+def run_prompt(case, p32=None, rows=None):
+    """Run a prompt case; ``rows`` = (a, b) runs only rows a..b-1 as their own call."""
+    from sliding_window_gqa_amd import api
+    p32 = case.p32 if p32 is None else p32
+    a, b = (0, case.n) if rows is None else rows
+    if case.buffer is not None:
+        buf = torch.from_numpy(case.buffer.view(np.int16)).view(torch.bfloat16).cuda()
+        q = dev_view(buf, case.q, case.buffer)[a:b]
+        k = dev_view(buf, case.k, case.buffer)
+        v = dev_view(buf, case.v, case.buffer)
+    else:
+        q = dev_bf16(case.q)[a:b]
+        k = dev_bf16(case.k)
+        v = dev_bf16(case.v)
+    hi = None if case.hi is None else dev_i32(case.hi[a:b])
+    out = api.prompt(q, k, v, case.p0 + a, case.win, case.ring, case.scale, hi=hi, p32=p32)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+def oracle_decode(case, rows=None):
+    return attend.decode(case.q, case.k, case.v, case.stream, case.pos, case.win, case.ring,
+                         case.scale, rows=rows)
+
+
+def oracle_prompt(case, rows=None):
+    return attend.prompt(case.q, case.k, case.v, case.p0, case.win, case.ring, case.scale,
+                         hi=case.hi, rows=rows)
+
+
+def compare(out, x, S, e_p, label):
+    """Gate: every output inside its tier-G interval. Logs the literal statistic."""
+    rep = check.report(out, x, S, e_p)
+    log(f"[{label}] n={rep['n']} equal={rep['equal']} within1ulp={rep['within_1ulp']} "
+        f"tierG_fail={rep['tier_G_fail']} tierS_fail={rep['tier_S_fail']}")
+    ok = check.accept(out, x, S, e_p, "G")
+    if not ok.all():
+        bad = np.argwhere(~ok)[:10]
+        for idx in bad:
+            t = tuple(idx)
+            log(f"  fail at {t}: out=0x{int(out[t]):04x} x={x[t]!r} S={S[t]!r}")
+    return rep, ok

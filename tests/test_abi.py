@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every entry point include/wa.h declares, sizes the decode
+workspace, and rejects host-checkable mistakes before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_gqa_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="libwa.so not built")
+
+WA_OK, WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE, WA_EHIP = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000  # never dereferenced: every call below returns before a launch
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(wa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) >= {"wa_decode", "wa_prompt", "wa_merge", "wa_decode_workspace",
+                          "wa_decode_chunks", "wa_status_string", "wa_version"}
+    L = ctypes.CDLL(api.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(api.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    L = api.lib()
+    assert b"gfx950" in L.wa_version()
+    for s in (WA_OK, WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE, WA_EHIP):
+        assert L.wa_status_string(s)
+    assert L.wa_status_string(12345) == b"unknown status"
+
+
+def test_chunks_and_workspace():
+    L = api.lib()
+    w = api.window(1024, 1536)
+    assert L.wa_decode_chunks(ctypes.byref(w), 40000) == 5
+    w64 = api.window(64, 300)
+    assert L.wa_decode_chunks(ctypes.byref(w64), 299) == 2
+    w256 = api.window(256, 300)
+    assert L.wa_decode_chunks(ctypes.byref(w256), 299) == 2
+    w257 = api.window(257, 300)            # keys lo..lo+256 touch at most 2 chunks
+    assert L.wa_decode_chunks(ctypes.byref(w257), 299) == 2
+    w258 = api.window(258, 300)            # lo = 255: keys 255..512 touch chunks 0, 1, 2
+    assert L.wa_decode_chunks(ctypes.byref(w258), 299) == 3
+    lin = api.window(0, 300)
+    assert L.wa_decode_chunks(ctypes.byref(lin), 299) == 2
+    assert L.wa_decode_chunks(ctypes.byref(lin), 255) == 1
+    # 64 rows x 16 heads x 5 chunks x (m, l, 256 dims) fp32
+    assert L.wa_decode_workspace(64, 16, 256, ctypes.byref(w), 0) == 64 * 16 * 5 * 258 * 4
+    assert L.wa_decode_workspace(64, 16, 100, ctypes.byref(w), 0) == 0
+    bad = api.window(-1, 10)
+    assert L.wa_decode_workspace(1, 1, 256, ctypes.byref(bad), 0) == 0
+
+
+def _decode(w, rows=2, hq=4, hkv=2, d=256, max_pos=100, ws_bytes=1 << 30, ptr=FAKE,
+            streams=1, strides=(1024, 256, 0, 512, 256)):
+    L = api.lib()
+    qs, qh, sst, ssl, sh = strides
+    return L.wa_decode(ctypes.byref(w), ptr, qs, qh, ptr, ptr, sst, ssl, sh, streams,
+                       ptr, ptr, max_pos, rows, hq, hkv, d, ptr, ws_bytes, ptr, qs, qh, None)
+
+
+def test_decode_rejects_before_launch():
+    w = api.window(64, 300)
+    assert _decode(w, ptr=None) == WA_EARG
+    assert _decode(w, rows=0) == WA_EARG
+    assert _decode(w, streams=0) == WA_EARG
+    assert _decode(w, d=64) == WA_EUNSUPPORTED
+    assert _decode(w, hq=6, hkv=4) == WA_EUNSUPPORTED
+    assert _decode(w, hq=34, hkv=2) == WA_EUNSUPPORTED        # group 17 > 16
+    assert _decode(api.window(-1, 300)) == WA_EARG
+    assert _decode(api.window(64, 0)) == WA_EARG
+    assert _decode(api.window(400, 300)) == WA_ERANGE          # window longer than the ring
+    assert _decode(api.window(0, 300), max_pos=300) == WA_ERANGE
+    assert _decode(w, ws_bytes=16) == WA_EWORKSPACE
+    assert _decode(w, strides=(1024, 250, 0, 512, 256)) == WA_EARG   # 16-byte rows
+    assert _decode(w, ptr=FAKE + 2) == WA_EARG                       # misaligned
+
+
+def _prompt(w, p0=0, n=10, hq=4, hkv=2, d=256, ptr=FAKE):
+    L = api.lib()
+    return L.wa_prompt(ctypes.byref(w), ptr, 1024, 256, ptr, ptr, 512, 256, p0, n, hq, hkv, d,
+                       None, ptr, 1024, 256, None)
+
+
+def test_prompt_rejects_before_launch():
+    w = api.window(1024, 1536)
+    assert _prompt(w, ptr=None) == WA_EARG
+    assert _prompt(w, n=0) == WA_EARG
+    assert _prompt(w, p0=-1) == WA_EARG
+    assert _prompt(w, d=192) == WA_EUNSUPPORTED
+    # ring must hold [p0 - window + 1, p0 + n - 1]: 513 + 1023 = 1536 keys fit, 514 do not
+    assert _prompt(w, p0=5000, n=514) == WA_ERANGE
+    assert _prompt(api.window(0, 100), p0=50, n=51) == WA_ERANGE
+    assert _prompt(w, ptr=FAKE + 8) == WA_EARG
+
+
+def test_merge_rejects_before_launch():
+    L = api.lib()
+    w = api.window(64, 300)
+    assert L.wa_merge(ctypes.byref(w), None, FAKE, FAKE, FAKE, 1, 1, 1, 256, FAKE, 1, 1, None) == WA_EARG
+    assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 96, FAKE, 1, 1, None) == WA_EUNSUPPORTED
+    assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 256, FAKE, 1, 1, None) == WA_EARG

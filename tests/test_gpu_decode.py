@@ -1,0 +1,214 @@
+"""GPU parity of the split-KV decode (wa_decode) against the float64 oracle.
+
+Gate: every bf16 output inside its tier-G interval (oracle.check) with fp32 probabilities
+(e_P = 0). Masks are pinned bit for bit by peaked-edge probes, accumulation by integer sums,
+and the row-bit invariants of TensorFold pull request #1123 ("Receipt", exactness bullet)
+by byte equality.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attend, check
+from sliding_window_gqa_amd import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+E_P = check.E_P_FP32
+
+
+def _gate(case, label, rows=None):
+    gu.log(f"decode case: {label} rows={case.rows} hq={case.hq} hkv={case.hkv} d={case.d} "
+           f"win={case.win} ring={case.ring}")
+    out = gu.run_decode(case)
+    x, S, _ = gu.oracle_decode(case)
+    rep, ok = gu.compare(out, x, S, E_P, label)
+    assert ok.all()
+    return out, rep
+
+
+def test_tiny_decode():
+    _gate(workloads.tiny_decode(), "tiny decode")
+
+
+def test_decode_12b_three_streams():
+    _, rep = _gate(workloads.decode_12b(), "12B decode 64 rows 3 streams")
+    assert rep["tier_S_fail"] <= rep["n"] // 1000
+
+
+def test_decode_12b_64_streams():
+    _gate(workloads.decode_12b(streams=64), "12B decode 64 rows 64 streams")
+
+
+SHAPES = [
+    # rows, hq, hkv, d, win, ring, streams
+    (5, 2, 1, 256, 1, 40, 1),
+    (7, 3, 1, 256, 300, 700, 2),
+    (9, 16, 2, 256, 1024, 1536, 3),
+    (6, 16, 1, 128, 257, 600, 2),
+    (4, 8, 8, 128, 64, 100, 4),
+    (3, 4, 2, 256, 0, 1300, 1),
+    (8, 32, 16, 256, 1024, 1536, 2),
+]
+
+
+@pytest.mark.parametrize("rows,hq,hkv,d,win,ring,streams", SHAPES)
+def test_decode_shapes(rows, hq, hkv, d, win, ring, streams):
+    rng = np.random.default_rng(rows * 131 + hq * 7 + d + win)
+    hi = ring - 1 if win == 0 else 3000
+    pos = rng.integers(0, hi + 1, size=rows)
+    pos[0] = 0
+    if rows > 2:
+        pos[1] = min(hi, 255)
+        pos[2] = min(hi, 256)
+    case = workloads.decode_case("shape", rows, hq, hkv, d, win, ring, streams, pos,
+                                 seed=rows + hq + d, peak_every=2)
+    _gate(case, f"decode shape {rows}x{hq}/{hkv}x{d} win{win} ring{ring}")
+
+
+def test_decode_invariants():
+    case = workloads.decode_12b()
+    full = gu.run_decode(case)
+    # each row alone, in another stream slot, at the same bits
+    for r in (0, 5, 17, 63):
+        t = int(case.stream[r])
+        k1 = case.k[t:t + 1].copy()
+        v1 = case.v[t:t + 1].copy()
+        one = workloads.DecodeCase("alone", case.q[r:r + 1], np.concatenate([k1 * 0, k1]),
+                                   np.concatenate([v1 * 0, v1]), np.array([1], np.int32),
+                                   case.pos[r:r + 1], case.win, case.ring)
+        assert np.array_equal(gu.run_decode(one)[0], full[r])
+    # a smaller call gives the widest call's bits
+    sub = workloads.DecodeCase("sub", case.q[10:27], case.k, case.v, case.stream[10:27],
+                               case.pos[10:27], case.win, case.ring)
+    assert np.array_equal(gu.run_decode(sub), full[10:27])
+    # repeat: byte-identical
+    for _ in range(4):
+        assert np.array_equal(gu.run_decode(case), full)
+
+
+def test_decode_linear_cache_declared_longer():
+    rows = 6
+    pos = np.array([0, 100, 255, 256, 700, 999])
+    base = workloads.decode_case("linear", rows, 4, 2, 256, 0, 1000, 1, pos, seed=5)
+    ref = gu.run_decode(base)
+    kl = np.zeros((1, 16000, 2, 256), np.uint16)
+    vl = np.zeros_like(kl)
+    kl[:, :1000] = base.k
+    vl[:, :1000] = base.v
+    longer = workloads.DecodeCase("linear x16", base.q, kl, vl, base.stream, base.pos, 0, 16000)
+    assert np.array_equal(gu.run_decode(longer), ref)
+    x, S, _ = gu.oracle_decode(base)
+    assert check.accept(ref, x, S, E_P).all()
+
+
+def _peak_row(case, r, key, vbits, gap_score=200.0):
+    """Make key ``key`` of row r's stream score ~gap_score for every head of the row."""
+    t = int(case.stream[r])
+    slot = key % case.ring
+    G = case.hq // case.hkv
+    for g in range(case.hkv):
+        qh = (case.q[r, g * G].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        case.k[t, slot, g] = workloads._bf16_bits(qh * (gap_score / (qh @ qh)))
+        case.v[t, slot, g] = vbits
+
+
+def test_decode_mask_edges_bit_exact():
+    """Peaked-edge probes: a key at lo and at pos must win outright (out == its v); a key at
+    lo - 1 or pos + 1 must not take part at all."""
+    win, ring, d = 1024, 1536, 256
+    rng = np.random.default_rng(21)
+    pos = np.array([1023, 1024, 2047, 5000, 40000, 256 * 57 + 255, 256 * 90, 300])
+    rows = len(pos)
+    for which in ("lo", "last", "lo-1", "last+1"):
+        case = workloads.decode_case("edges", rows, 2, 1, d, win, ring, rows, pos, seed=3,
+                                     peak_every=0, stream=np.arange(rows))
+        # G = 2 query heads share key head 0: make both heads point the same way
+        case.q[:, 1] = case.q[:, 0]
+        marks = []
+        for r in range(rows):
+            lo, last = attend.key_window(int(pos[r]), win)
+            key = {"lo": lo, "last": last, "lo-1": lo - 1, "last+1": last + 1}[which]
+            if key < 0:
+                marks.append(None)
+                continue
+            vb = workloads._bf16_bits(rng.standard_normal(d) * 4)
+            _peak_row(case, r, key, vb)
+            marks.append(vb)
+        out = gu.run_decode(case)
+        x, S, _ = gu.oracle_decode(case)
+        assert check.accept(out, x, S, E_P).all(), which
+        for r, vb in enumerate(marks):
+            if vb is None:
+                continue
+            hit = np.array_equal(out[r, 0], vb) and np.array_equal(out[r, 1], vb)
+            assert hit == (which in ("lo", "last")), (which, r)
+
+
+def test_decode_integer_sums():
+    """Every key alike: every weight is exactly 1, so the output is the exact mean of the
+    visible integer values. Values 96..127 make an fp16 running sum overflow and a bf16 one
+    drop integers; fp32 holds them exactly."""
+    rows, d, win, ring = 3, 256, 1024, 1536
+    pos = np.array([1023, 4000, 1500])
+    case = workloads.decode_case("sums", rows, 2, 1, d, win, ring, 1, pos, seed=4, peak_every=0)
+    case.k[:] = case.k[0, 0, 0]
+    slot_vals = 96.0 + (np.arange(ring) * 7) % 32
+    case.v[0, :, 0] = workloads._bf16_bits(slot_vals[:, None] * np.ones(d))
+    out = gu.run_decode(case)
+    for r in range(rows):
+        lo, last = attend.key_window(int(pos[r]), win)
+        mean = slot_vals[np.arange(lo, last + 1) % ring].sum() / (last - lo + 1)
+        want = workloads._bf16_bits(np.array([np.float32(mean)]))[0]
+        assert np.all(out[r] == want), r
+
+
+def _nf_case():
+    pos = np.array([100, 300, 301, 600])
+    return workloads.decode_case("nonfinite", 4, 4, 2, 256, 256, 700, 1, pos, seed=9, peak_every=0)
+
+
+def test_decode_nonfinite_classes():
+    NAN, PINF, NINF = 0x7FC0, 0x7F80, 0xFF80
+    # NaN query: that (row, head) only
+    c = _nf_case()
+    c.q[1, 2, 7] = NAN
+    out = gu.run_decode(c)
+    x, S, _ = gu.oracle_decode(c)
+    assert check.accept(out, x, S, E_P).all()
+    assert np.isnan(x[1, 2]).all()
+    # a visible NaN key: the group's heads of the rows that see it
+    c = _nf_case()
+    c.k[0, 301 % 700, 1, 3] = NAN
+    out = gu.run_decode(c)
+    x, S, _ = gu.oracle_decode(c)
+    assert check.accept(out, x, S, E_P).all()
+    # +inf in a value only later rows see
+    c = _nf_case()
+    c.v[0, 301, 0, 9] = PINF
+    out = gu.run_decode(c)
+    x, S, _ = gu.oracle_decode(c)
+    assert check.accept(out, x, S, E_P).all()
+    assert np.isinf(x[2, 0:2, 9]).all() and np.isfinite(x[[0, 1, 3]]).all()
+    # +inf and -inf in one column
+    c = _nf_case()
+    c.v[0, 290, 1, 4] = PINF
+    c.v[0, 291, 1, 4] = NINF
+    out = gu.run_decode(c)
+    x, S, _ = gu.oracle_decode(c)
+    assert check.accept(out, x, S, E_P).all()
+
+
+@pytest.mark.xfail(reason="fp32 weights underflow to 0 where float64's e^-200 is not; "
+                          "needs the float64 re-run of non-finite rows", strict=True)
+def test_decode_inf_at_negligible_key():
+    c = workloads.decode_case("e-200", 1, 1, 1, 256, 4, 16, 1, [10], seed=2, peak_every=0)
+    c.q[0, 0] = workloads._bf16_bits(np.full(256, 1.0))
+    c.k[0, 7, 0] = workloads._bf16_bits(np.full(256, 200.0 / 256))
+    c.k[0, 8, 0] = workloads._bf16_bits(np.zeros(256))
+    c.v[0, 8, 0, 3] = 0x7F80
+    out = gu.run_decode(c)
+    x, S, _ = gu.oracle_decode(c)
+    assert check.accept(out, x, S, E_P).all()
