@@ -76,23 +76,31 @@ __device__ __forceinline__ int wave_max_i(int x) {
     return x;
 }
 
-template <int D>
-struct TileRegs {
-    static constexpr int KV = BN * D / 8 / kThreads;   // 16-byte K chunks per thread
-    static constexpr int VV = BN * D / 8 / kThreads;   // 16-byte V chunks per thread
-    uint4 k[KV];
-    uint4 v[VV];
-};
+// Chunk swizzle of the LDS tiles: 16-byte chunk c of row r sits at position
+// c ^ swz(r) (low four bits). It makes the K reads of the S^T product (16 rows with
+// distinct low bits) and the transposing V reads (4 consecutive rows x 4 chunks) fall on
+// distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <int D, bool P32>
 __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(PromptArgs a, int nblk) {
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
-    constexpr int KS = D + 8;      // K tile row stride (elements)
-    constexpr int VS = BN + 8;     // V^T tile row stride (elements)
-    constexpr int DC = D / 8;      // 16-byte chunks per key row
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t VT[2][D * VS];
+    constexpr int RB = 2 * D;              // bytes per K/V row in LDS
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPK = 1024 / RB;         // rows per 1 KiB wave load
+    constexpr int NQ = BN * RB / 1024;     // 1 KiB wave loads per tile (each of K and V)
+    constexpr int TILE_B = BN * RB;        // bytes of one K (or V) tile
+    // two stages of K and V tiles, as four distinct arrays so that the compiler can tell
+    // the direct-to-LDS loads into one stage from the reads of the other
+    __shared__ __attribute__((aligned(1024))) char Ks0[TILE_B];
+    __shared__ __attribute__((aligned(1024))) char Vs0[TILE_B];
+    __shared__ __attribute__((aligned(1024))) char Ks1[TILE_B];
+    __shared__ __attribute__((aligned(1024))) char Vs1[TILE_B];
     __shared__ int red_i[2][kWaves];
 
     // XCD-aware remap of the linear workgroup index
@@ -140,9 +148,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     for (int w = 1; w < kWaves; ++w) { kmin = min(kmin, red_i[0][w]); kmax = max(kmax, red_i[1][w]); }
     if (kmax < kmin) return;                // no valid pair in this workgroup
 
-    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7
-    // A negative scale is carried by q's sign (exact), so the exponent factor is positive
-    // and the row maximum of the raw scores gives the maximum of the scaled ones.
+    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7. A negative scale is carried
+    // by q's sign (exact), so the exponent factor is positive and the row maximum of the
+    // raw scores gives the maximum of the scaled ones.
     Pack8 qreg[KSTEPS];
     {
         const uint16_t* qp = a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
@@ -165,77 +173,56 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 
     const uint16_t* kg = a.k + (int64_t)g * a.kv_shead;
     const uint16_t* vg = a.v + (int64_t)g * a.kv_shead;
-    const int krow = sigma(col);            // K row this lane feeds to the S^T MFMA
 
-    // this thread's share of a tile load: K row chunks (coalesced rows), V 4-key groups
-    const int k_dc = tid % DC, k_kk0 = tid / DC;          // K: key k_kk0 + it*(kThreads/DC)
-    constexpr int KSTRIDE = kThreads / DC;
-    const int v_dc = tid % DC, v_kq0 = tid / DC;          // V: keys 4*(v_kq0 + it*KSTRIDE) + 0..3
+    // LDS read offsets (bytes within a tile), fixed for the whole key loop.
+    // K for S^T: row 32*mb + sigma(col), logical chunk 2*ks + h.
+    const int krow = sigma(col);
+    int koff[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int c = 2 * ks + h;
+        koff[ks] = krow * RB + 16 * ((c & ~15) | ((c & 15) ^ swz(krow)));
+    }
+    // V for O^T via the transposing read: 16-lane group q = lane / 16, j = lane % 16 reads
+    // row 16*s + 8*h + 4*u + j/4 at dims 32*db + 16*(q & 1) + 4*(j & 3) + 0..3.
+    const int j16 = lane & 15, cg = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    int voff[2][DBLK];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int vr = 8 * h + 4 * u + (j16 >> 2);      // row within a 16-key step (s = 0)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const int c = 4 * db + cg;
+            voff[u][db] = vr * RB + 16 * ((c & ~15) | ((c & 15) ^ swz(vr))) + 8 * (j16 & 1);
+        }
+    }
 
-    auto load_tile = [&](int tile, TileRegs<D>& r) {
+    // One wave load moves 1 KiB: RPK rows of CPR chunks; lane -> (row, stored chunk p),
+    // fetching logical chunk p ^ swz(row) of key base + row (clamped into [kmin, kmax], so
+    // every fetched key is one the ring holds; keys outside every window are masked).
+    const int ld_row = lane / CPR, ld_p = lane % CPR;
+    auto issue_tile = [&](int tile, char* kdst, char* vdst) {
         const int base = tile * BN;
-        int sbase = base % a.ring;
+        const int sbase = base % a.ring;
 #pragma unroll
-        for (int it = 0; it < TileRegs<D>::KV; ++it) {
-            const int kk = k_kk0 + it * KSTRIDE;
-            const int j = base + kk;
-            int s = sbase + kk;
-            s = s >= a.ring ? s - a.ring : s;
-            r.k[it] = make_uint4(0, 0, 0, 0);
-            if (j >= kmin && j <= kmax)
-                r.k[it] = *reinterpret_cast<const uint4*>(kg + (int64_t)s * a.kv_sslot + k_dc * 8);
-        }
-#pragma unroll
-        for (int it = 0; it < TileRegs<D>::VV; ++it) {
-            const int kk = 4 * v_kq0 + (it / 4) * 4 * KSTRIDE + (it % 4);
-            const int j = base + kk;
-            int s = sbase + kk;
-            s = s >= a.ring ? s - a.ring : s;
-            r.v[it] = make_uint4(0, 0, 0, 0);
-            if (j >= kmin && j <= kmax)
-                r.v[it] = *reinterpret_cast<const uint4*>(vg + (int64_t)s * a.kv_sslot + v_dc * 8);
-        }
-    };
-    auto store_tile = [&](int buf, const TileRegs<D>& r) {
-#pragma unroll
-        for (int it = 0; it < TileRegs<D>::KV; ++it) {
-            const int kk = k_kk0 + it * KSTRIDE;
-            *reinterpret_cast<uint4*>(&Ks[buf][kk * KS + k_dc * 8]) = r.k[it];
-        }
-#pragma unroll
-        for (int grp = 0; grp < TileRegs<D>::VV / 4; ++grp) {
-            const int kk = 4 * v_kq0 + grp * 4 * KSTRIDE;
-            const uint4* x = &r.v[grp * 4];
-            const uint32_t w0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
-            const uint32_t w1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
-            const uint32_t w2[4] = {x[2].x, x[2].y, x[2].z, x[2].w};
-            const uint32_t w3[4] = {x[3].x, x[3].y, x[3].z, x[3].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // dims 2e and 2e+1 of keys kk..kk+3
-                uint2 lo2, hi2;
-                lo2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-                lo2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x05040100u);
-                hi2.x = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-                hi2.y = __builtin_amdgcn_perm(w3[e], w2[e], 0x07060302u);
-                *reinterpret_cast<uint2*>(&VT[buf][(v_dc * 8 + 2 * e) * VS + kk]) = lo2;
-                *reinterpret_cast<uint2*>(&VT[buf][(v_dc * 8 + 2 * e + 1) * VS + kk]) = hi2;
-            }
+        for (int i = 0; i < NQ / kWaves; ++i) {
+            const int q = wave + kWaves * i;
+            const int r = RPK * q + ld_row;
+            const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
+            const int jc = min(max(base + r, kmin), kmax);
+            int slot = sbase + (jc - base);
+            slot = slot >= a.ring ? slot - a.ring : slot;
+            const int64_t off = (int64_t)slot * a.kv_sslot + 8 * c;
+            __builtin_amdgcn_global_load_lds(kg + off, (lds_void_ptr)(kdst + 1024 * q), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg + off, (lds_void_ptr)(vdst + 1024 * q), 16, 0, 0);
         }
     };
 
-    const int t0 = kmin / BN, t1 = kmax / BN;
-    TileRegs<D> pre;
-    load_tile(t0, pre);
-    store_tile(0, pre);
-    __syncthreads();
-
-    for (int tile = t0; tile <= t1; ++tile) {
-        const int buf = (tile - t0) & 1;
+    // one tile: start the next tile's loads into the other stage, compute on this stage,
+    // then wait for the loads and meet at the barrier
+    auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more) {
         const int base = tile * BN;
-        const bool more = tile < t1;
-        if (more) load_tile(tile + 1, pre);
-
+        if (more) issue_tile(tile + 1, knext, vnext);
         // this wave computes only if the tile meets its key range
         if (base <= w_kmax && base + BN - 1 >= w_kmin) {
             // S^T = K Q^T for two 32-key halves
@@ -244,11 +231,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
-                const uint16_t* kp = &Ks[buf][(32 * mb + krow) * KS + 8 * h];
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     Pack8 av;
-                    av.u = *reinterpret_cast<const uint4*>(kp + 16 * ks);
+                    av.u = *reinterpret_cast<const uint4*>(kt + 32 * mb * RB + koff[ks]);
                     sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, qreg[ks].v, sacc[mb], 0, 0, 0);
                 }
             }
@@ -292,7 +278,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             l_run += psum;
             m_run = m_new;
 
-            // O^T += V^T P^T, four 16-key steps
+            // O^T += V^T P^T, four 16-key steps; V^T comes from the transposing LDS read
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int mb = s >> 1, r0 = (s & 1) * 8;
@@ -305,16 +291,32 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
                 }
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db) {
+                    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_ptr)(vt + 16 * s * RB + voff[0][db]));
+                    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_ptr)(vt + 16 * s * RB + voff[1][db]));
                     Pack8 av;
-                    av.u = *reinterpret_cast<const uint4*>(&VT[buf][(32 * db + col) * VS + 16 * s + 8 * h]);
+                    av.w[0] = __builtin_bit_cast(uint2, x0).x;
+                    av.w[1] = __builtin_bit_cast(uint2, x0).y;
+                    av.w[2] = __builtin_bit_cast(uint2, x1).x;
+                    av.w[3] = __builtin_bit_cast(uint2, x1).y;
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
                     if (P32)
                         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
                 }
             }
         }
-        if (more) store_tile(buf ^ 1, pre);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    const int t0 = kmin / BN, t1 = kmax / BN;
+    issue_tile(t0, Ks0, Vs0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int tile = t0; tile <= t1; tile += 2) {
+        step(tile, Ks0, Vs0, Ks1, Vs1, tile < t1);
+        if (tile + 1 <= t1) step(tile + 1, Ks1, Vs1, Ks0, Vs0, tile + 1 < t1);
     }
 
     // epilogue: O / l, one rounding to bf16
