@@ -193,6 +193,29 @@ def cpu_baseline(case, budget_s=10.0):
                       f"(numpy float64, BLAS threads as shown)"}
 
 
+def profile_driver(names, iters):
+    """Run the workloads for profiler passes, after a plain copy of known size."""
+    a = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)                     # 256 MiB read + 256 MiB written: counter calibration
+    torch.cuda.synchronize()
+    del a, b
+    make = {"decode12b": lambda: Decoder(workloads.decode_12b()),
+            "decode12b64": lambda: Decoder(workloads.decode_12b(streams=64)),
+            "prompt12b": lambda: Prompter(workloads.prompt_12b()),
+            "prompt31b": lambda: Prompter(workloads.prompt_31b()),
+            "long": lambda: Prompter(workloads.long_prompt())}
+    for n in names:
+        f = make[n]()
+        torch.cuda.synchronize()
+        for _ in range(iters):
+            f()
+        torch.cuda.synchronize()
+        print("done", n, flush=True)
+        del f
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +224,10 @@ def main():
     ap.add_argument("--long-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profiler driver: run a 256 MiB device copy (counter calibration), then "
+                         "each listed workload (decode12b, decode12b64, prompt12b, prompt31b, "
+                         "long) --steps times; no timing, no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -208,6 +235,9 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     api.lib()
+    if args.only:
+        profile_driver(args.only.split(","), args.steps)
+        return
 
     dcase = workloads.decode_12b()
     pcase = workloads.prompt_12b()
