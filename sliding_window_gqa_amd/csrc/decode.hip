@@ -9,13 +9,35 @@
 // split depends only on key positions.
 //
 // gfx950 mapping (wave64):
-//   scores  D/8 lanes per key, each lane an fma chain over 8 consecutive dims of the key
-//           (one 16-byte load), then a xor butterfly across those lanes; 64/(D/8) keys per
-//           wave instruction, coalesced 16-byte loads of each key row.
+//   scores  v_mfma_f32_16x16x32_bf16 with the chunk's keys on M and the group's query heads
+//           on N (up to 16); bf16 x bf16 products are exact in fp32, the sums are fp32. K
+//           rows go straight from HBM/L2 into the MFMA operand registers (128 contiguous
+//           bytes per lane); each wave scores 64 keys.
 //   softmax one wave per query head: 4 keys per lane, wave butterflies for max and sum.
-//   P.V     NRUN key runs of 256/NRUN consecutive keys; D/8 lanes per run, 8 dims a lane;
-//           each run is an fma chain in key order; runs are summed in run order through LDS.
+//   P.V     fp32 on the VALU: NRUN key runs of 256/NRUN consecutive keys; D/8 lanes per
+//           run, 8 dims a lane; each run is an fma chain in key order; runs are summed in
+//           run order through LDS.
+//   grid    one workgroup per (row, key head, chunk), ordered so that each XCD works on the
+//           rows of a few key heads and their rings stay in its L2.
 #include "wa_common.h"
+
+// Tuning switches (defaults chosen by measurement on MI355X):
+//   WA_DECODE_ORDER   0: XCD-grouped (key head, row, chunk) order; 1: (row, chunk, key head)
+//   WA_DECODE_VEARLY  1: issue the V loads before the score MFMAs wait for K
+//   WA_DECODE_KT      16-key K tiles in flight together per wave (4 tiles per wave)
+//   WA_DECODE_VB      batches the V loads of a key run are split into (register budget)
+#ifndef WA_DECODE_ORDER
+#define WA_DECODE_ORDER 0
+#endif
+#ifndef WA_DECODE_VEARLY
+#define WA_DECODE_VEARLY 0
+#endif
+#ifndef WA_DECODE_KT
+#define WA_DECODE_KT 2
+#endif
+#ifndef WA_DECODE_VB
+#define WA_DECODE_VB 2
+#endif
 
 namespace wa {
 
@@ -60,21 +82,50 @@ __device__ __forceinline__ RowSpan row_span(const int32_t* pos_of_row, int r, in
     return s;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+union Pack8 {
+    bf16x8 v;
+    uint4 u;
+};
+
+// Linear workgroup id -> logical id such that each XCD (8 on MI355X, ids dealt out
+// round-robin) runs a contiguous range of logical ids.
+__device__ __forceinline__ int xcd_logical(int L, int total) {
+    const int xcd = L & 7, idx = L >> 3;
+    const int per = total >> 3, extra = total & 7;
+    return (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + idx;
+}
+
 template <int D, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_part_kernel(DecodeArgs a) {
-    constexpr int LPK = D / 8;           // lanes per key in the score pass
-    constexpr int KPW = 64 / LPK;        // keys per wave instruction
+    constexpr int KSTEPS = D / 32;       // MFMA k-steps over the head dim
+    constexpr int LPK = D / 8;           // lanes per key run row in P.V (8 dims a lane)
     constexpr int NRUN = kThreads / LPK; // P.V key runs
     constexpr int RUNLEN = kChunk / NRUN;
     constexpr int GH = GMAX < 4 ? GMAX : 4;   // heads per LDS reduction pass
+    constexpr int NB = WA_DECODE_VB;          // V prefetch batches per run (register budget)
+    constexpr int BL = RUNLEN / NB;           // keys per batch
 
-    __shared__ float qs[GMAX][D];
     __shared__ float sc[GMAX][kChunk];
     __shared__ float red[NRUN][GH][D];
 
-    const int kslot = blockIdx.x;
-    const int g = blockIdx.y;
-    const int r = blockIdx.z;
+#if WA_DECODE_ORDER == 0
+    // logical order (key head, row, chunk slot): an XCD holds the rows of a few key heads
+    const int total = gridDim.x;
+    const int logical = xcd_logical(blockIdx.x, total);
+    const int per_g = a.rows * a.C;
+    const int g = logical / per_g;
+    const int r = (logical % per_g) / a.C;
+    const int kslot = logical % a.C;
+#else
+    // order (row, chunk slot, key head), key heads adjacent, no XCD remap
+    const int logical = blockIdx.x;
+    const int g = logical % a.hkv;
+    const int kslot = (logical / a.hkv) % a.C;
+    const int r = logical / (a.hkv * a.C);
+#endif
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -82,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(DecodeArgs a) {
 
     const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
     const int c = rs.c_lo + kslot;
-    if (c > rs.c_hi || kslot >= a.C) return;
+    if (c > rs.c_hi) return;
     int t = a.stream_of_row[r];
     t = t < 0 ? 0 : (t >= a.streams ? a.streams - 1 : t);
     const int j0 = max(rs.lo, c * kChunk);
@@ -92,45 +143,85 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(DecodeArgs a) {
 
     const uint16_t* kbase_ptr = a.k + (int64_t)t * a.kv_sstream + (int64_t)g * a.kv_shead;
     const uint16_t* vbase_ptr = a.v + (int64_t)t * a.kv_sstream + (int64_t)g * a.kv_shead;
+    // ring slot of chunk-relative key kk: one modulo per workgroup, then a conditional
+    // subtraction (a ring of at least one chunk wraps at most once inside a chunk)
+    const int sb = (c * kChunk) % a.ring;
+    const bool big_ring = a.ring >= kChunk;
+    auto slot_of = [&](int kk) {
+        const int s = sb + kk;
+        return big_ring ? (s >= a.ring ? s - a.ring : s) : s % a.ring;
+    };
 
-    // q of the group's heads, widened to fp32
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, e = i % D;
-        qs[h][e] = bf16_to_f32(a.q[(int64_t)r * a.q_srow + (int64_t)(g * G + h) * a.q_shead + e]);
-    }
-    __syncthreads();
+    // ---- start this thread's V loads for P.V now, so their latency hides behind the
+    // softmax: run `run` covers chunk keys run*RUNLEN .. +RUNLEN-1, 8 dims per lane
+    const int run = tid / LPK;
+    const int dl = tid % LPK;
+    const int r0 = max(run * RUNLEN, kbase);
+    const int r1 = min(run * RUNLEN + RUNLEN, kbase + nk);
+    uint4 vr[BL];
+    // whole-run loads: every key of a run that holds a visible key is fetched (its slot is
+    // inside the ring), keys outside [r0, r1) are skipped in the sums below
+    auto load_batch = [&](int b) {
+        if (r0 < r1) {
+#pragma unroll
+            for (int i = 0; i < BL; ++i) {
+                const int slot = slot_of(run * RUNLEN + b * BL + i);
+                vr[i] = *reinterpret_cast<const uint4*>(vbase_ptr + (int64_t)slot * a.kv_sslot + dl * 8);
+            }
+        }
+    };
+#if WA_DECODE_VEARLY
+    load_batch(0);
+#endif
 
-    // ---- scores: s = scale * (q . k) for the visible keys ----
+    // ---- scores on MFMA: S^T (16 keys x 16 heads) = K (16 x 32 dims) . q^T, fp32 accumulate.
+    // bf16 x bf16 products are exact in fp32; only the sum is rounded. Lane l feeds key
+    // l % 16 of the tile and dims 32*ks + 8*(l/16) + 0..7 at k-step ks (the four lanes of a
+    // key read 64 contiguous bytes per instruction; the q operand uses the same dims); the
+    // result lane holds head l % 16 and keys 4*(l/16) + 0..3 of the tile. Wave w scores
+    // chunk keys 64w .. 64w+63.
     {
-        const int sub = lane / LPK;          // key within the wave instruction
-        const int dl = lane % LPK;           // 8-dim slice of the key
-        float qf[GMAX][8];
+        const int n = lane & 15, kg = lane >> 4;
+        Pack8 qb[KSTEPS];
+        // lanes of heads >= G read head G-1 and their scores are never used
+        const uint16_t* qp = a.q + (int64_t)r * a.q_srow + (int64_t)(g * G + min(n, G - 1)) * a.q_shead + 8 * kg;
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h)
+        for (int ks = 0; ks < KSTEPS; ++ks) qb[ks].u = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+        const int kw0 = 64 * wave;                        // chunk-relative first key of the wave
+        if (kw0 < kbase + nk && kw0 + 63 >= kbase) {
+            constexpr int KT = WA_DECODE_KT;              // 16-key tiles whose K is in flight together
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[h][e] = (h < G) ? qs[h][dl * 8 + e] : 0.f;
-        for (int base = wave * KPW; base < nk; base += 4 * KPW) {
-            const int kk = base + sub;
-            const bool valid = kk < nk;
-            const int j = j0 + (valid ? kk : 0);
-            const int slot = j % a.ring;
-            float kf[8];
-            load8(kbase_ptr + (int64_t)slot * a.kv_sslot + dl * 8, kf);
+            for (int u0 = 0; u0 < 4; u0 += KT) {
+                Pack8 kb[KT][KSTEPS];
 #pragma unroll
-            for (int h = 0; h < GMAX; ++h) {
-                if (h < G) {
-                    float s = 0.f;
+                for (int u = 0; u < KT; ++u) {
+                    const int slot = slot_of(kw0 + 16 * (u0 + u) + n);
+                    const uint16_t* kp = kbase_ptr + (int64_t)slot * a.kv_sslot + 8 * kg;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) s = fmaf(qf[h][e], kf[e], s);
+                    for (int ks = 0; ks < KSTEPS; ++ks) kb[u][ks].u = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+                }
 #pragma unroll
-                    for (int m = 1; m < LPK; m <<= 1) s += xor_shfl(s, m);
-                    if (valid && dl == 0) sc[h][kbase + kk] = a.scale * s;
+                for (int u = 0; u < KT; ++u) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[u][ks].v, qb[ks].v, acc, 0, 0, 0);
+                    if (n < G) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int kk = kw0 + 16 * (u0 + u) + 4 * kg + i;
+                            if (kk >= kbase && kk < kbase + nk) sc[n][kk] = a.scale * acc[i];
+                        }
+                    }
                 }
             }
         }
     }
-    __syncthreads();
 
+#if !WA_DECODE_VEARLY
+    load_batch(0);
+#endif
+    __syncthreads();
     // ---- chunk softmax: m_c, p = expf(s - m_c), l_c, one wave per head ----
     for (int h = wave; h < G; h += 4) {
         float mx = -INFINITY;
@@ -161,27 +252,36 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(DecodeArgs a) {
     __syncthreads();
 
     // ---- P.V: NRUN runs of consecutive keys, fma chains in key order ----
-    const int run = tid / LPK;
-    const int dl = tid % LPK;
     float acc[GMAX][8];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    {
-        const int r0 = max(run * RUNLEN, kbase);
-        const int r1 = min(run * RUNLEN + RUNLEN, kbase + nk);
-        for (int kk = r0; kk < r1; ++kk) {
-            const int slot = (c * kChunk + kk) % a.ring;
-            float vf[8];
-            load8(vbase_ptr + (int64_t)slot * a.kv_sslot + dl * 8, vf);
+    const bool run_full = r0 == run * RUNLEN && r1 == run * RUNLEN + RUNLEN;
+    auto fold_key = [&](int i, int kk) {
+        const uint4 w = vr[i];
+        const float vf[8] = {lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y),
+                             lo_bf16(w.z), hi_bf16(w.z), lo_bf16(w.w), hi_bf16(w.w)};
 #pragma unroll
-            for (int h = 0; h < GMAX; ++h) {
-                if (h < G) {
-                    const float p = sc[h][kk];
+        for (int h = 0; h < GMAX; ++h) {
+            if (h < G) {
+                const float p = sc[h][kk];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-                }
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+            }
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if (b > 0) load_batch(b);
+        if (run_full) {
+#pragma unroll
+            for (int i = 0; i < BL; ++i) fold_key(i, run * RUNLEN + b * BL + i);
+        } else if (r0 < r1) {
+#pragma unroll
+            for (int i = 0; i < BL; ++i) {
+                const int kk = run * RUNLEN + b * BL + i;
+                if (kk >= r0 && kk < r1) fold_key(i, kk);
             }
         }
     }
@@ -231,7 +331,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
 template <int D>
 hipError_t launch_part_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
-    dim3 grid(a.C, a.hkv, a.rows);
+    dim3 grid(a.C * a.hkv * a.rows);
     if (G <= 1) hipLaunchKernelGGL((decode_part_kernel<D, 1>), grid, dim3(kThreads), 0, s, a);
     else if (G <= 2) hipLaunchKernelGGL((decode_part_kernel<D, 2>), grid, dim3(kThreads), 0, s, a);
     else if (G <= 4) hipLaunchKernelGGL((decode_part_kernel<D, 4>), grid, dim3(kThreads), 0, s, a);
