@@ -165,6 +165,32 @@ class Prompter:
             raise RuntimeError(f"wa_prompt status {st}")
 
 
+def source_hash():
+    import hashlib
+    import glob
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sliding_window_gqa_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload, kernels):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
+    profiles/traffic.txt for these kernels, or None if the kernel sources changed since."""
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.txt")))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    tot, found = 0, False
+    for name, v in t.get("workloads", {}).get(workload, {}).items():
+        if any(k in name for k in kernels):
+            tot += v.get("fetch", 0) + v.get("write", 0)
+            found = True
+    return tot if found else None
+
+
 def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -308,8 +334,10 @@ def main():
                     "flop_accounting": "(2 + 2*2) * d per visible (row, head, key), p32"},
         "wall_s_timed_loop": round(wall, 3),
     }
-    rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s")
-    rl_decode = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
+    rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s",
+                         traffic_bytes("prompt12b", ["prompt_kernel"]))
+    rl_decode = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                         traffic_bytes("decode12b", ["decode_part_kernel", "merge_kernel"]))
     rl_prompt["kernel"] = "prompt_kernel<256,p32> (12B prompt chunk)"
     rl_decode["kernel"] = "decode_part_kernel<256,2> + merge_kernel<256> (unique K/V bytes)"
     res["roofline"] = rl_prompt if pms >= dms else rl_decode
@@ -318,7 +346,8 @@ def main():
     res["decode_64_streams"] = {"workload": "12B decode shape, 64 rows in 64 streams (no shared keys)",
                                 "ms": round(hms, 5), "bytes_per_call": hu["row_bytes"],
                                 "gbs": round(hgbs, 2)}
-    rl_h = roofline("hbm", hgbs, HBM_PEAK_GBS, "GB/s")
+    rl_h = roofline("hbm", hgbs, HBM_PEAK_GBS, "GB/s",
+                    traffic_bytes("decode12b64", ["decode_part_kernel", "merge_kernel"]))
     rl_h["kernel"] = "decode_part_kernel<256,2> + merge_kernel<256> (64 streams)"
     res["roofline_decode_64_streams"] = rl_h
 
@@ -336,7 +365,8 @@ def main():
         res["prefill_long"] = {"workload": "long non-windowed prompt 37,810 x 56 x 128, non-causal, bf16 P",
                                "ms": round(lms, 3), "tflops": round(ltf, 2),
                                "flops_per_call": lu["flops"]}
-        rl = roofline("mfma", ltf, MFMA_BF16_PEAK_TFS, "TFLOP/s")
+        rl = roofline("mfma", ltf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
+                      traffic_bytes("long", ["prompt_kernel"]))
         rl["kernel"] = "prompt_kernel<128,bf16P> (long prompt)"
         res["roofline_prefill_long"] = rl
         del lp
