@@ -150,11 +150,15 @@ class Prompter:
         self.out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
         api.prompt(self.q, self.k, self.v, case.p0, case.win, case.ring, case.scale, hi=self.hi,
                    p32=case.p32, out=self.out)
+        torch.cuda.synchronize()
         self.w = api.window(case.win, case.ring, case.scale, case.p32)
+        need = api.prompt_workspace_bytes(case.n, case.hq, case.d, case.win, case.ring)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         q, k = self.q, self.k
         self.args = (ctypes.byref(self.w), q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(),
                      self.v.data_ptr(), k.stride(0), k.stride(1), case.p0, case.n, case.hq,
                      case.hkv, case.d, None if self.hi is None else self.hi.data_ptr(),
+                     self.ws.data_ptr(), self.ws.numel(),
                      self.out.data_ptr(), self.out.stride(0), self.out.stride(1),
                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         self.fn = api.lib().wa_prompt

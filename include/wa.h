@@ -21,6 +21,7 @@
  *   prompt  rows p0 .. p0+n-1 of one stream, tiled online softmax on MFMA (bf16 products,
  *           fp32 accumulation), key tiles at absolute positions ("Prompt" bullet); P enters
  *           P.V as one bf16, or with p32 as bf16(P) + bf16(P - bf16(P)) ("Window.p32" bullet).
+ *           Windowed prompts are also split into 256-key chunks merged in chunk order.
  *           A row's bits do not depend on how the prompt is chunked.
  *
  * Conventions for every entry point:
@@ -116,23 +117,36 @@ int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* 
              const int32_t* pos_of_row, int32_t rows, int32_t hq, int32_t C, int32_t d,
              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
+/* Bytes of device workspace wa_prompt needs: 0 for window == 0; otherwise fp32 partials
+ * m, l [n][hq][Cp] and o [n][hq][Cp][d] with Cp = (window - 1 + n) / 256 + 2, plus 16 bytes
+ * of alignment slack. 0 on invalid arguments (and for window == 0). */
+size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t d);
+
 /*
  * Prompt: rows i = 0 .. n-1 at positions p0 + i of one stream. Row i sees keys
  * [lo_i, last_i] with last_i = hi[i] if hi is not NULL (device int32 [n],
  * p0 + i <= hi[i] < p0 + n), else p0 + i.
  *   q        [n][hq][d]       strides q_srow, q_shead
  *   k, v     [ring][hkv][d]   strides kv_sslot, kv_shead (one stream's ring)
+ *   ws       device workspace, 16-byte aligned, of ws_bytes >= wa_prompt_workspace(w, n, hq, d)
+ *            (may be NULL when window == 0)
  *   out      [n][hq][d]       strides o_srow, o_shead
+ * With a window (> 0) the keys of every row are split into 256-key chunks at absolute
+ * positions: one tiled online softmax per chunk gives fp32 partials (m in log2 units, l, O),
+ * and a merge combines a row's chunks in chunk order (the decode's split applied to the
+ * prompt, so that short windowed prompts fill the GPU); window 0 runs one online softmax over
+ * the row's whole key range. Either way a row's bits depend only on its own keys and the
+ * absolute chunk and tile grid, not on how the prompt is cut into calls.
  * The ring must hold keys [min lo_i, p0 + n - 1] without two of them sharing a slot:
  * ring >= p0 + n - max(0, p0 - window + 1) (window > 0) or ring >= p0 + n (window == 0),
  * else WA_ERANGE. hi values out of range are clamped into [p0 + i, p0 + n - 1].
- * Errors: WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EHIP.
+ * Errors: WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE, WA_EHIP.
  */
 int wa_prompt(const wa_window_t* w,
               const uint16_t* q, int64_t q_srow, int64_t q_shead,
               const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
               int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
-              const int32_t* hi,
+              const int32_t* hi, void* ws, size_t ws_bytes,
               uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
 /* Human-readable name of a status code (static storage). */

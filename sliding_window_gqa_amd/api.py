@@ -41,8 +41,9 @@ SIGNATURES = {
                                  _P, _I64, _I64, _P]),
     "wa_merge": (ctypes.c_int, [_WP, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                 _P, _I64, _I64, _P]),
+    "wa_prompt_workspace": (_SZ, [_WP, _I32, _I32, _I32]),
     "wa_prompt": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64,
-                                 _I32, _I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P]),
+                                 _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _I64, _I64, _P]),
     "wa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "wa_version": (ctypes.c_char_p, []),
 }
@@ -135,7 +136,12 @@ def merge(m, l, o, pos_of_row, win, ring, out=None):
     return out
 
 
-def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None):
+def prompt_workspace_bytes(n, hq, d, win, ring):
+    w = window(win, ring)
+    return lib().wa_prompt_workspace(ctypes.byref(w), n, hq, d)
+
+
+def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None, workspace=None):
     """Prompt rows p0 .. p0+n-1. q [n, Hq, d]; k, v [ring, Hkv, d] (bf16, CUDA, any
     strides with a unit dim stride); hi int32 [n] (CUDA) or None."""
     _bf16(q, "q"); _bf16(k, "k"); _bf16(v, "v")
@@ -152,8 +158,13 @@ def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None):
     if out is None:
         out = torch.empty((n, hq, d), dtype=torch.bfloat16, device=q.device)
     w = window(win, ring, scale, p32)
+    need = lib().wa_prompt_workspace(ctypes.byref(w), n, hq, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
     _check(lib().wa_prompt(ctypes.byref(w), q.data_ptr(), q.stride(0), q.stride(1),
                            k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
-                           int(p0), n, hq, hkv, d, hp, out.data_ptr(), out.stride(0),
+                           int(p0), n, hq, hkv, d, hp, wp, wn, out.data_ptr(), out.stride(0),
                            out.stride(1), _stream()))
     return out

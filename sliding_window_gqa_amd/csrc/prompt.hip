@@ -109,8 +109,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     const int xcd = L & 7, idx = L >> 3;
     const int per = total >> 3, extra = total & 7;
     const int logical = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + idx;
-    const int g = logical / nblk;           // key head
-    const int blk = logical % nblk;         // block of pairs
+    const int cidx = logical % a.nchunk;    // key chunk of the workgroup's range (split mode)
+    const int gb = logical / a.nchunk;
+    const int g = gb / nblk;                // key head
+    const int blk = gb % nblk;              // block of pairs
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,6 +149,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) { kmin = min(kmin, red_i[0][w]); kmax = max(kmax, red_i[1][w]); }
     if (kmax < kmin) return;                // no valid pair in this workgroup
+    // split mode: this workgroup takes the 256-key chunk cidx of its range, at absolute
+    // positions, and writes per-chunk partials that a merge combines in chunk order
+    const bool split = a.nchunk > 1;
+    const int chunk = kmin / kPromptChunk + cidx;
+    if (split) {
+        kmin = max(kmin, chunk * kPromptChunk);
+        kmax = min(kmax, chunk * kPromptChunk + kPromptChunk - 1);
+        if (kmax < kmin) return;
+    }
 
     // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7. A negative scale is carried
     // by q's sign (exact), so the exponent factor is positive and the row maximum of the
@@ -319,8 +330,24 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         if (tile + 1 <= t1) step(tile + 1, Ks1, Vs1, Ks0, Vs0, tile + 1 < t1);
     }
 
-    // epilogue: O / l, one rounding to bf16
+    // epilogue: O / l, one rounding to bf16; in split mode the chunk's (m, l, O) partial
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (split) {
+        if (valid && lo <= chunk * kPromptChunk + kPromptChunk - 1 && last >= chunk * kPromptChunk) {
+            const int64_t pi = ((int64_t)row * a.hq + head) * a.Cp + (chunk - lo / kPromptChunk);
+            if (h == 0) { a.pm[pi] = m_run; a.pl[pi] = l_tot; }
+            float* op = a.po + pi * D;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * db + 8 * q4 + 4 * h;
+                    *reinterpret_cast<float4*>(op + d0) =
+                        make_float4(oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]);
+                }
+        }
+        return;
+    }
     if (valid) {
         uint16_t* op = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
 #pragma unroll
@@ -336,13 +363,45 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     }
 }
 
+// Merge of the split prompt's chunk partials, one workgroup per (row, head), one thread per
+// dim: chunks of the row's range in order, M = max m_c, a_c = 2^(m_c - M) (m is in log2
+// units), out = bf16(sum a_c o_c / sum a_c l_c), both sums fma chains in chunk order.
+template <int D>
+__global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
+    const int row = blockIdx.x;
+    const int head = blockIdx.y;
+    const int e = threadIdx.x;
+    const int p = a.p0 + row;
+    const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+    int last = p;
+    if (a.hi) {
+        int hv = a.hi[row];
+        last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+    }
+    int nc = last / kPromptChunk - lo / kPromptChunk + 1;
+    nc = nc > a.Cp ? a.Cp : nc;
+    const int64_t pi = ((int64_t)row * a.hq + head) * a.Cp;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.pm[pi + c]);
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float ac = __builtin_amdgcn_exp2f(a.pm[pi + c] - M);
+        num = fmaf(ac, a.po[(pi + c) * D + e], num);
+        den = fmaf(ac, a.pl[pi + c], den);
+    }
+    a.out[(int64_t)row * a.o_srow + (int64_t)head * a.o_shead + e] = (uint16_t)f32_to_bf16_rne(num / den);
+}
+
 template <int D>
 hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPairs - 1) / kPairs);
-    dim3 grid(nblk * a.hkv);
+    dim3 grid(nblk * a.hkv * a.nchunk);
     if (a.p32) hipLaunchKernelGGL((prompt_kernel<D, true>), grid, dim3(kThreads), 0, s, a, nblk);
     else hipLaunchKernelGGL((prompt_kernel<D, false>), grid, dim3(kThreads), 0, s, a, nblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nchunk <= 1) return e;
+    hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
     return hipGetLastError();
 }
 

@@ -95,11 +95,18 @@ int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* 
     return WA_OK;
 }
 
+size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t d) {
+    if (!window_ok(w) || n <= 0 || hq <= 0 || (d != 128 && d != 256)) return 0;
+    if (w->window == 0) return 0;
+    const size_t cells = (size_t)n * (size_t)hq * (size_t)wa::prompt_pair_chunks(w->window, n);
+    return cells * sizeof(float) * (2 + (size_t)d) + 16;   // + alignment slack of the O block
+}
+
 int wa_prompt(const wa_window_t* w,
               const uint16_t* q, int64_t q_srow, int64_t q_shead,
               const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
               int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
-              const int32_t* hi,
+              const int32_t* hi, void* ws, size_t ws_bytes,
               uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
     if (!w || !q || !k || !v || !out) return WA_EARG;
     if (n <= 0 || p0 < 0) return WA_EARG;
@@ -107,7 +114,7 @@ int wa_prompt(const wa_window_t* w,
         return WA_EARG;
     if (!head_shape_ok(hq, hkv, d)) return WA_EUNSUPPORTED;
     if (!window_ok(w)) return WA_EARG;
-    if ((int64_t)p0 + n > 0x7FFFFFFF) return WA_ERANGE;
+    if ((int64_t)p0 + n > 0x7FFFFFFF || (int64_t)n + w->window > 0x3FFFFFFF) return WA_ERANGE;
     const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
     if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
@@ -121,6 +128,20 @@ int wa_prompt(const wa_window_t* w,
     a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p32 = w->p32 != 0;
     a.hi = hi;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    a.nchunk = 1; a.Cp = 0; a.pm = a.pl = a.po = nullptr;
+    if (w->window > 0) {
+        const size_t need = wa_prompt_workspace(w, n, hq, d);
+        if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return WA_EWORKSPACE;
+        a.nchunk = wa::prompt_wg_chunks(w->window, n);
+        a.Cp = wa::prompt_pair_chunks(w->window, n);
+        const size_t cells = (size_t)n * hq * a.Cp;
+        a.pm = static_cast<float*>(ws);
+        a.pl = a.pm + cells;
+        a.po = a.pl + cells;
+        // 16-byte stores of the O partials: the O block starts 16-byte aligned when
+        // 2 * cells floats are a multiple of 4, otherwise shift it
+        if (((uintptr_t)a.po) & 15) a.po = reinterpret_cast<float*>(((uintptr_t)a.po + 15) & ~(uintptr_t)15);
+    }
     if (wa::launch_prompt(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
     return WA_OK;
 }

@@ -53,7 +53,19 @@ struct PromptArgs {
     int32_t window, ring; float scale; int32_t p32;
     const int32_t* hi;
     uint16_t* out; int64_t o_srow, o_shead;
+    // key-chunk split (windowed prompts): nchunk = 256-key chunks per workgroup grid slot
+    // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials
+    int32_t nchunk, Cp;
+    float* pm; float* pl; float* po;
 };
+
+constexpr int kPromptChunk = 256;   // prompt split: keys [256c, 256c + 255], absolute
+
+// Chunk capacities of the windowed-prompt split (both are bounds, independent of the data):
+// chunks a workgroup's key range can touch, and chunks one row's key range can touch
+// (a row's last key is at most p0 + n - 1, so its range spans at most window - 1 + n keys).
+inline int prompt_wg_chunks(int window, int n) { return (window - 1 + n) / kPromptChunk + 2; }
+inline int prompt_pair_chunks(int window, int n) { return (window - 1 + n) / kPromptChunk + 2; }
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_decode_part(const DecodeArgs& a, hipStream_t s);

@@ -88,10 +88,10 @@ def test_decode_rejects_before_launch():
     assert _decode(w, ptr=FAKE + 2) == WA_EARG                       # misaligned
 
 
-def _prompt(w, p0=0, n=10, hq=4, hkv=2, d=256, ptr=FAKE):
+def _prompt(w, p0=0, n=10, hq=4, hkv=2, d=256, ptr=FAKE, ws_bytes=1 << 30):
     L = api.lib()
     return L.wa_prompt(ctypes.byref(w), ptr, 1024, 256, ptr, ptr, 512, 256, p0, n, hq, hkv, d,
-                       None, ptr, 1024, 256, None)
+                       None, ptr, ws_bytes, ptr, 1024, 256, None)
 
 
 def test_prompt_rejects_before_launch():
@@ -104,6 +104,16 @@ def test_prompt_rejects_before_launch():
     assert _prompt(w, p0=5000, n=514) == WA_ERANGE
     assert _prompt(api.window(0, 100), p0=50, n=51) == WA_ERANGE
     assert _prompt(w, ptr=FAKE + 8) == WA_EARG
+    assert _prompt(w, ws_bytes=64) == WA_EWORKSPACE             # windowed: chunk partials
+
+
+def test_prompt_workspace_sizes():
+    L = api.lib()
+    w = api.window(1024, 1536)
+    # 512 rows x 16 heads x ((1023 + 512) / 256 + 2 = 7 chunks) x (m, l, 256 dims) + slack
+    assert L.wa_prompt_workspace(ctypes.byref(w), 512, 16, 256) == 512 * 16 * 7 * 258 * 4 + 16
+    assert L.wa_prompt_workspace(ctypes.byref(api.window(0, 4096)), 512, 16, 256) == 0
+    assert L.wa_prompt_workspace(ctypes.byref(w), 512, 16, 64) == 0
 
 
 def test_merge_rejects_before_launch():
