@@ -20,6 +20,7 @@
 //   grid    one workgroup per (row, key head, chunk), ordered so that each XCD works on the
 //           rows of a few key heads and their rings stay in its L2.
 #include "wa_common.h"
+#include "rerun_f64.h"
 
 // Tuning switches (defaults chosen by measurement on MI355X):
 //   WA_DECODE_ORDER   0: XCD-grouped (key head, row, chunk) order; 1: (row, chunk, key head)
@@ -325,7 +326,17 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
         num = fmaf(ac, a.o[(pi + c) * D + e], num);
         den = fmaf(ac, a.l[pi + c], den);
     }
-    a.out[(int64_t)r * a.o_srow + (int64_t)h * a.o_shead + e] = (uint16_t)f32_to_bf16_rne(num / den);
+    uint16_t* orow = a.out + (int64_t)r * a.o_srow + (int64_t)h * a.o_shead;
+    orow[e] = (uint16_t)f32_to_bf16_rne(num / den);
+    // a NaN or infinity anywhere in this (row, head): its float64 re-run
+    if (a.rerun && any_nonfinite<D>(orow)) {
+        int t = a.stream_of_row[r];
+        t = t < 0 ? 0 : (t >= a.streams ? a.streams - 1 : t);
+        const int g = h / (a.hq / a.hkv);
+        const int64_t kv = (int64_t)t * a.kv_sstream + (int64_t)g * a.kv_shead;
+        rerun_f64<D>(a.q + (int64_t)r * a.q_srow + (int64_t)h * a.q_shead, a.k + kv, a.v + kv,
+                     a.kv_sslot, a.ring, rs.lo, rs.pos, a.scale, orow);
+    }
 }
 
 template <int D>

@@ -29,6 +29,7 @@
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
 //     a key head's K/V stream in that XCD's L2.
 #include "wa_common.h"
+#include "rerun_f64.h"
 
 namespace wa {
 
@@ -389,7 +390,33 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         num = fmaf(ac, a.po[(pi + c) * D + e], num);
         den = fmaf(ac, a.pl[pi + c], den);
     }
-    a.out[(int64_t)row * a.o_srow + (int64_t)head * a.o_shead + e] = (uint16_t)f32_to_bf16_rne(num / den);
+    uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
+    orow[e] = (uint16_t)f32_to_bf16_rne(num / den);
+    if (any_nonfinite<D>(orow)) {
+        const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
+        rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
+                     a.kv_sslot, a.ring, lo, last, a.scale, orow);
+    }
+}
+
+// Unsplit prompts: find the (row, head)s whose bf16 output holds a NaN or an infinity and
+// re-run each of them alone in float64; every other (row, head) is only read.
+template <int D>
+__global__ __launch_bounds__(D) void prompt_check_kernel(PromptArgs a) {
+    const int row = blockIdx.x;
+    const int head = blockIdx.y;
+    uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
+    if (!any_nonfinite<D>(orow)) return;
+    const int p = a.p0 + row;
+    const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+    int last = p;
+    if (a.hi) {
+        int hv = a.hi[row];
+        last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+    }
+    const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
+    rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
+                 a.kv_sslot, a.ring, lo, last, a.scale, orow);
 }
 
 template <int D>
@@ -400,8 +427,9 @@ hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     if (a.p32) hipLaunchKernelGGL((prompt_kernel<D, true>), grid, dim3(kThreads), 0, s, a, nblk);
     else hipLaunchKernelGGL((prompt_kernel<D, false>), grid, dim3(kThreads), 0, s, a, nblk);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nchunk <= 1) return e;
-    hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
+    if (e != hipSuccess) return e;
+    if (a.nchunk > 1) hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
+    else hipLaunchKernelGGL((prompt_check_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
     return hipGetLastError();
 }
 

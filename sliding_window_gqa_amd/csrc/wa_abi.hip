@@ -72,6 +72,7 @@ int wa_decode(const wa_window_t* w,
     a.l = a.m + cells;
     a.o = a.l + cells;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    a.rerun = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (wa::launch_decode_part(a, s) != hipSuccess) return WA_EHIP;
     if (wa::launch_merge(a, s) != hipSuccess) return WA_EHIP;
@@ -91,6 +92,7 @@ int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* 
     a.window = w->window; a.ring = w->ring; a.scale = w->scale;
     a.max_pos = 0x7FFFFFFF;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    a.rerun = 0;   // no q/K/V here: partials made elsewhere are merged as they are
     if (wa::launch_merge(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
     return WA_OK;
 }

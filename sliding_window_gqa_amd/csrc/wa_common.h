@@ -43,6 +43,7 @@ struct DecodeArgs {
     int32_t window, ring; float scale;
     int32_t C;                    // chunk capacity of the partial arrays
     float* m; float* l; float* o; // partials
+    int32_t rerun;                // 1: re-run non-finite (row, head)s in float64 after the merge
     uint16_t* out; int64_t o_srow, o_shead;
 };
 
