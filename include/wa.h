@@ -38,10 +38,12 @@
  *     preconditions (positions, stream indices, hi) cannot be checked without a
  *     synchronisation; the kernels clamp them into range so that every access stays inside
  *     the caller's buffers, and the result for a violating row is then unspecified.
- *   - Until the float64 re-run of non-finite rows exists, a non-finite output has the class
- *     that fp32 arithmetic gives. That is float64's class except where a weight that float64
- *     keeps underflows to zero in fp32 beside an infinite value (0 * inf), or where finite
- *     inputs overflow fp32 in q . k.
+ *   - Non-finite outputs take float64's class: wa_decode and wa_prompt re-run, in float64,
+ *     exactly the (row, head)s whose bf16 output holds a NaN or an infinity (the pull
+ *     request's non-finite bullet and review: per row and head, never per block). fp32 can
+ *     differ from float64 only there (a weight that underflows to 0 beside an infinite value,
+ *     0 * inf in a shared MFMA tile, fp32 overflow of q . k). wa_merge alone does not re-run
+ *     (it has no q, K, V).
  */
 #ifndef WA_H
 #define WA_H
