@@ -238,18 +238,38 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         // this wave computes only if the tile meets its key range
         if (base <= w_kmax && base + BN - 1 >= w_kmin) {
             // S^T = K Q^T for two 32-key halves
+            // the two 32-key halves alternate, so each LDS read has two MFMAs to hide behind
             f32x16 sacc[2];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
+            // K fragments are read two k-steps ahead of their MFMAs
+            Pack8 ka[2][2];
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    Pack8 av;
-                    av.u = *reinterpret_cast<const uint4*>(kt + 32 * mb * RB + koff[ks]);
-                    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, qreg[ks].v, sacc[mb], 0, 0, 0);
-                }
+            for (int ks = 0; ks < 2; ++ks) {
+                ka[ks][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks]);
+                ka[ks][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks]);
             }
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const Pack8 a0 = ka[ks & 1][0], a1 = ka[ks & 1][1];
+                if (ks + 2 < KSTEPS) {
+                    ka[ks & 1][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks + 2]);
+                    ka[ks & 1][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks + 2]);
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0.v, qreg[ks].v, sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1.v, qreg[ks].v, sacc[1], 0, 0, 0);
+            }
+            // keep the reads two k-steps ahead in the instruction order: 4 reads, then
+            // (2 MFMAs, 2 reads) pairs, then the last 4 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int ks = 0; ks + 2 < KSTEPS; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
             // online softmax; t = s * scale * log2(e) is formed inside the exponent's fma
             const bool full = base >= w_loall && base + BN - 1 <= w_lastall;
