@@ -77,7 +77,10 @@ enum {
 int32_t wa_decode_chunks(const wa_window_t* w, int32_t max_pos);
 
 /* Bytes of device workspace wa_decode needs for `rows` rows of `hq` heads of dim `d`:
- * fp32 partials m, l [rows][hq][C] and o [rows][hq][C][d], C = wa_decode_chunks(). 0 on error. */
+ * fp32 partials m, l [rows][hq][C] and o [rows][hq][C][d], C = wa_decode_chunks(). With
+ * cells = rows * hq * C rounded up to even, m starts at the workspace, l at float offset
+ * cells and o at float offset 2 * cells (so o is 16-byte aligned, as wa_merge needs).
+ * 0 on error. */
 size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_t* w,
                            int32_t max_pos);
 
@@ -88,7 +91,8 @@ size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_
  *   q        [rows][hq][d]          strides q_srow, q_shead
  *   k, v     [streams][ring][hkv][d] strides kv_sstream, kv_sslot, kv_shead
  *   max_pos  an upper bound of every pos_of_row[r] (sizes the chunk grid when window == 0)
- *   ws       device workspace of ws_bytes >= wa_decode_workspace(rows, hq, d, w, max_pos)
+ *   ws       device workspace, 16-byte aligned, of ws_bytes >= wa_decode_workspace(rows, hq,
+ *            d, w, max_pos); after the call it holds the chunk partials in the layout above
  *   out      [rows][hq][d]          strides o_srow, o_shead
  * Device preconditions: 0 <= pos_of_row[r] <= max_pos, 0 <= stream_of_row[r] < streams, and
  * the ring holds keys [lo_r, pos_r] of row r's stream in slots j mod ring. Errors: WA_EARG,
@@ -111,9 +115,9 @@ int wa_decode(const wa_window_t* w,
  * the number of 256-key chunks holding keys [lo_r, pos_r] (pos from pos_of_row), in chunk
  * order: M = max m_c, a_c = exp(m_c - M), out = bf16(sum a_c o_c / sum a_c l_c), both sums
  * fma chains over the chunks in order ("Decode" bullet of the pull request).
- *   m, l  [rows][hq][C] fp32      o  [rows][hq][C][d] fp32       C = chunk capacity
+ *   m, l  [rows][hq][C] fp32      o  [rows][hq][C][d] fp32 (16-byte aligned)   C = chunk capacity
  * Device precondition: n_r <= C (rows violating it read only their first C chunks).
- * Errors: WA_EARG, WA_EUNSUPPORTED, WA_EHIP.
+ * Errors: WA_EARG (also for an o that is not 16-byte aligned), WA_EUNSUPPORTED, WA_EHIP.
  */
 int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* o,
              const int32_t* pos_of_row, int32_t rows, int32_t hq, int32_t C, int32_t d,

@@ -308,34 +308,97 @@ __global__ __launch_bounds__(kThreads) void decode_part_kernel(DecodeArgs a) {
     }
 }
 
-// One workgroup per (row, query head); one thread per output dim.
+// Ordered merge: M = max m_c over the row's chunks, a_c = expf(m_c - M), out = bf16(sum a_c o_c /
+// sum a_c l_c), both sums fma chains in chunk order. One wave per (row, query head): lane c
+// holds chunk c's (m, l), lane i dims DL*i .. DL*i + DL - 1. (row, head)s with a non-finite
+// output are listed and, when the caller passed q/K/V, re-run in float64 afterwards by the
+// whole workgroup.
+constexpr int kMergePairs = 4;     // = waves of a D = 256 workgroup; D = 128 loops twice
+
 template <int D>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
-    const int r = blockIdx.x;
-    const int h = blockIdx.y;
-    const int e = threadIdx.x;
-    const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
-    int n = rs.c_hi - rs.c_lo + 1;
-    n = n > a.C ? a.C : n;
-    const int64_t pi = ((int64_t)r * a.hq + h) * a.C;
-    float M = -INFINITY;
-    for (int c = 0; c < n; ++c) M = fmaxf(M, a.m[pi + c]);
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < n; ++c) {
-        const float ac = expf(a.m[pi + c] - M);
-        num = fmaf(ac, a.o[(pi + c) * D + e], num);
-        den = fmaf(ac, a.l[pi + c], den);
+    constexpr int W = D / 64;             // waves
+    constexpr int DL = D / 64;            // dims per lane
+    __shared__ int flagged[kMergePairs];
+    __shared__ int nflag;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t npairs = (int64_t)a.rows * a.hq;
+    const int64_t first = (int64_t)blockIdx.x * kMergePairs;
+    if (t == 0) nflag = 0;
+    __syncthreads();
+    for (int i = wave; i < kMergePairs; i += W) {
+        const int64_t pr = first + i;
+        if (pr >= npairs) break;
+        const int r = (int)(pr / a.hq), h = (int)(pr % a.hq);
+        const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
+        int n = rs.c_hi - rs.c_lo + 1;
+        n = n > a.C ? a.C : n;
+        const int64_t pi = pr * a.C;      // (r * hq + h) * C
+        float M = -INFINITY;
+        for (int cb = 0; cb < n; cb += 64)
+            M = fmaxf(M, cb + lane < n ? a.m[pi + cb + lane] : -INFINITY);
+        M = wave_max(M);
+        float num[DL], den = 0.f;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) num[e] = 0.f;
+        const float* op = a.o + pi * D + DL * lane;
+        for (int cb = 0; cb < n; cb += 64) {
+            const bool in = cb + lane < n;
+            const float ac = expf((in ? a.m[pi + cb + lane] : -INFINITY) - M);
+            const float lc = in ? a.l[pi + cb + lane] : 0.f;
+            const int ce = min(n - cb, 64);
+            // eight chunks' o loads in flight at a time, then their fmas in chunk order
+            for (int cg = 0; cg < ce; cg += 8) {
+                float o[8][DL];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (cg + j < ce) {
+                        const float* oc = op + (int64_t)(cb + cg + j) * D;
+                        if constexpr (DL == 4) {
+                            const float4 v = *reinterpret_cast<const float4*>(oc);
+                            o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
+                        } else {
+                            const float2 v = *reinterpret_cast<const float2*>(oc);
+                            o[j][0] = v.x; o[j][1] = v.y;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (cg + j < ce) {
+                        const float ac_c = __shfl(ac, cg + j, 64);
+                        const float l_c = __shfl(lc, cg + j, 64);
+#pragma unroll
+                        for (int e = 0; e < DL; ++e) num[e] = fmaf(ac_c, o[j][e], num[e]);
+                        den = fmaf(ac_c, l_c, den);
+                    }
+                }
+            }
+        }
+        uint16_t* orow = a.out + (int64_t)r * a.o_srow + (int64_t)h * a.o_shead;
+        bool bad = false;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+            const uint32_t b = f32_to_bf16_rne(num[e] / den);
+            orow[DL * lane + e] = (uint16_t)b;
+            bad = bad || bf16_nonfinite((uint16_t)b);
+        }
+        if (a.rerun && __any(bad) && lane == 0) flagged[atomicAdd(&nflag, 1)] = i;
     }
-    uint16_t* orow = a.out + (int64_t)r * a.o_srow + (int64_t)h * a.o_shead;
-    orow[e] = (uint16_t)f32_to_bf16_rne(num / den);
-    // a NaN or infinity anywhere in this (row, head): its float64 re-run
-    if (a.rerun && any_nonfinite<D>(orow)) {
-        int t = a.stream_of_row[r];
-        t = t < 0 ? 0 : (t >= a.streams ? a.streams - 1 : t);
+    __syncthreads();
+    const int nf = nflag;
+    for (int f = 0; f < nf; ++f) {
+        const int64_t pr = first + flagged[f];
+        const int r = (int)(pr / a.hq), h = (int)(pr % a.hq);
+        const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
+        int t_ = a.stream_of_row[r];
+        t_ = t_ < 0 ? 0 : (t_ >= a.streams ? a.streams - 1 : t_);
         const int g = h / (a.hq / a.hkv);
-        const int64_t kv = (int64_t)t * a.kv_sstream + (int64_t)g * a.kv_shead;
+        const int64_t kv = (int64_t)t_ * a.kv_sstream + (int64_t)g * a.kv_shead;
+        uint16_t* orow = a.out + (int64_t)r * a.o_srow + (int64_t)h * a.o_shead;
         rerun_f64<D>(a.q + (int64_t)r * a.q_srow + (int64_t)h * a.q_shead, a.k + kv, a.v + kv,
                      a.kv_sslot, a.ring, rs.lo, rs.pos, a.scale, orow);
+        __syncthreads();
     }
 }
 
@@ -358,7 +421,7 @@ hipError_t launch_decode_part(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid(a.rows, a.hq);
+    dim3 grid((unsigned)(((int64_t)a.rows * a.hq + kMergePairs - 1) / kMergePairs));
     if (a.d == 256) hipLaunchKernelGGL((merge_kernel<256>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(128), 0, s, a);
     return hipGetLastError();

@@ -384,59 +384,169 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     }
 }
 
-// Merge of the split prompt's chunk partials, one workgroup per (row, head), one thread per
-// dim: chunks of the row's range in order, M = max m_c, a_c = 2^(m_c - M) (m is in log2
-// units), out = bf16(sum a_c o_c / sum a_c l_c), both sums fma chains in chunk order.
+// Merge of the split prompt's chunk partials: M = max m_c over the chunks of the row's range,
+// a_c = 2^(m_c - M) (m is in log2 units), out = bf16(sum a_c o_c / sum a_c l_c), both sums
+// fma chains in chunk order. One wave per (row, head): lane c holds chunk c's (m, l), lane i
+// dims DL*i .. DL*i + DL - 1. (row, head)s with a non-finite output are listed and re-run in
+// float64 afterwards by the whole workgroup.
+constexpr int kMergePairs = 4;     // = waves of a D = 256 workgroup; D = 128 loops twice
+
 template <int D>
 __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
-    const int row = blockIdx.x;
-    const int head = blockIdx.y;
-    const int e = threadIdx.x;
-    const int p = a.p0 + row;
-    const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-    int last = p;
-    if (a.hi) {
-        int hv = a.hi[row];
-        last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+    constexpr int W = D / 64;             // waves
+    constexpr int DL = D / 64;            // dims per lane
+    __shared__ int flagged[kMergePairs];
+    __shared__ int nflag;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t npairs = (int64_t)a.n * a.hq;
+    const int64_t first = (int64_t)blockIdx.x * kMergePairs;
+    if (t == 0) nflag = 0;
+    __syncthreads();
+    for (int i = wave; i < kMergePairs; i += W) {
+        const int64_t pr = first + i;
+        if (pr >= npairs) break;
+        const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
+        const int p = a.p0 + row;
+        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+        int last = p;
+        if (a.hi) {
+            const int hv = a.hi[row];
+            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+        }
+        int nc = last / kPromptChunk - lo / kPromptChunk + 1;
+        nc = nc > a.Cp ? a.Cp : nc;
+        const int64_t pi = pr * a.Cp;     // (row * hq + head) * Cp
+        // chunks in blocks of 64, lane c of a block holding chunk (m, l)
+        float M = -INFINITY;
+        for (int cb = 0; cb < nc; cb += 64)
+            M = fmaxf(M, cb + lane < nc ? a.pm[pi + cb + lane] : -INFINITY);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+        float num[DL], den = 0.f;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) num[e] = 0.f;
+        const float* op = a.po + pi * D + DL * lane;
+        for (int cb = 0; cb < nc; cb += 64) {
+            const bool in = cb + lane < nc;
+            const float ac = __builtin_amdgcn_exp2f((in ? a.pm[pi + cb + lane] : -INFINITY) - M);
+            const float lc = in ? a.pl[pi + cb + lane] : 0.f;
+            const int ce = min(nc - cb, 64);
+            // eight chunks' o loads in flight at a time, then their fmas in chunk order
+            for (int cg = 0; cg < ce; cg += 8) {
+                float o[8][DL];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (cg + j < ce) {
+                        const float* oc = op + (int64_t)(cb + cg + j) * D;
+                        if constexpr (DL == 4) {
+                            const float4 v = *reinterpret_cast<const float4*>(oc);
+                            o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
+                        } else {
+                            const float2 v = *reinterpret_cast<const float2*>(oc);
+                            o[j][0] = v.x; o[j][1] = v.y;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (cg + j < ce) {
+                        const float ac_c = __shfl(ac, cg + j, 64);
+                        const float l_c = __shfl(lc, cg + j, 64);
+#pragma unroll
+                        for (int e = 0; e < DL; ++e) num[e] = fmaf(ac_c, o[j][e], num[e]);
+                        den = fmaf(ac_c, l_c, den);
+                    }
+                }
+            }
+        }
+        uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
+        uint32_t b[DL];
+        bool bad = false;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+            b[e] = f32_to_bf16_rne(num[e] / den);
+            bad = bad || bf16_nonfinite((uint16_t)b[e]);
+        }
+        if constexpr (DL == 4) {
+            *reinterpret_cast<uint2*>(orow + DL * lane) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        } else {
+            *reinterpret_cast<uint32_t*>(orow + DL * lane) = b[0] | (b[1] << 16);
+        }
+        if (__any(bad) && lane == 0) flagged[atomicAdd(&nflag, 1)] = i;
     }
-    int nc = last / kPromptChunk - lo / kPromptChunk + 1;
-    nc = nc > a.Cp ? a.Cp : nc;
-    const int64_t pi = ((int64_t)row * a.hq + head) * a.Cp;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.pm[pi + c]);
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float ac = __builtin_amdgcn_exp2f(a.pm[pi + c] - M);
-        num = fmaf(ac, a.po[(pi + c) * D + e], num);
-        den = fmaf(ac, a.pl[pi + c], den);
-    }
-    uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
-    orow[e] = (uint16_t)f32_to_bf16_rne(num / den);
-    if (any_nonfinite<D>(orow)) {
+    __syncthreads();
+    const int nf = nflag;
+    for (int f = 0; f < nf; ++f) {
+        const int64_t pr = first + flagged[f];
+        const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
+        const int p = a.p0 + row;
+        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+        int last = p;
+        if (a.hi) {
+            const int hv = a.hi[row];
+            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+        }
+        uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
         const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
         rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
                      a.kv_sslot, a.ring, lo, last, a.scale, orow);
+        __syncthreads();
     }
 }
 
 // Unsplit prompts: find the (row, head)s whose bf16 output holds a NaN or an infinity and
-// re-run each of them alone in float64; every other (row, head) is only read.
+// re-run each of them alone in float64; every other (row, head) is only read. A workgroup
+// scans kCheckPairs consecutive (row, head)s, 4 bf16 a lane, then re-runs the flagged ones
+// one after the other with all its threads.
+constexpr int kCheckPairs = 64;
+
 template <int D>
 __global__ __launch_bounds__(D) void prompt_check_kernel(PromptArgs a) {
-    const int row = blockIdx.x;
-    const int head = blockIdx.y;
-    uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
-    if (!any_nonfinite<D>(orow)) return;
-    const int p = a.p0 + row;
-    const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-    int last = p;
-    if (a.hi) {
-        int hv = a.hi[row];
-        last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+    constexpr int TPP = D / 4;            // lanes per (row, head): 4 bf16 each
+    constexpr int PPI = D / TPP;          // (row, head)s per pass of the workgroup
+    __shared__ int flagged[kCheckPairs];
+    __shared__ int nflag;
+    const int t = threadIdx.x;
+    const int64_t npairs = (int64_t)a.n * a.hq;
+    const int64_t first = (int64_t)blockIdx.x * kCheckPairs;
+    if (t == 0) nflag = 0;
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < kCheckPairs / PPI; ++it) {
+        const int local = it * PPI + t / TPP;
+        const int64_t pr = first + local;
+        bool bad = false;
+        if (pr < npairs) {
+            const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
+            const uint2 w = *reinterpret_cast<const uint2*>(
+                a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead + 4 * (t % TPP));
+            bad = bf16_nonfinite(w.x & 0xFFFFu) || bf16_nonfinite(w.x >> 16) ||
+                  bf16_nonfinite(w.y & 0xFFFFu) || bf16_nonfinite(w.y >> 16);
+        }
+        // OR over the TPP lanes of each (row, head); TPP divides the wave
+        const unsigned long long b = __ballot(bad);
+        const int sub = (t & 63) / TPP;
+        const unsigned long long m = TPP == 64 ? ~0ull : (((1ull << TPP) - 1) << (sub * TPP));
+        if ((b & m) != 0 && t % TPP == 0) flagged[atomicAdd(&nflag, 1)] = local;
     }
-    const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
-    rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
-                 a.kv_sslot, a.ring, lo, last, a.scale, orow);
+    __syncthreads();
+    const int nf = nflag;
+    for (int i = 0; i < nf; ++i) {
+        const int64_t pr = first + flagged[i];
+        const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
+        uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
+        const int p = a.p0 + row;
+        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+        int last = p;
+        if (a.hi) {
+            int hv = a.hi[row];
+            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+        }
+        const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
+        rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
+                     a.kv_sslot, a.ring, lo, last, a.scale, orow);
+        __syncthreads();
+    }
 }
 
 template <int D>
@@ -448,8 +558,14 @@ hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL((prompt_kernel<D, false>), grid, dim3(kThreads), 0, s, a, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.nchunk > 1) hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
-    else hipLaunchKernelGGL((prompt_check_kernel<D>), dim3(a.n, a.hq), dim3(D), 0, s, a);
+    const int64_t npairs = (int64_t)a.n * a.hq;
+    if (a.nchunk > 1)
+        hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3((unsigned)((npairs + kMergePairs - 1) / kMergePairs)),
+                           dim3(D), 0, s, a);
+    else {
+        hipLaunchKernelGGL((prompt_check_kernel<D>), dim3((unsigned)((npairs + kCheckPairs - 1) / kCheckPairs)),
+                           dim3(D), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -34,7 +34,9 @@ size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_
     const int C = chunk_capacity(w, max_pos);
     if (C <= 0 || rows <= 0 || hq <= 0 || (d != 128 && d != 256)) return 0;
     const size_t cells = (size_t)rows * (size_t)hq * (size_t)C;
-    return cells * sizeof(float) * (2 + (size_t)d);
+    // m and l take an even number of floats each, so that o starts 16-byte aligned
+    const size_t cells2 = (cells + 1) & ~(size_t)1;
+    return (2 * cells2 + cells * (size_t)d) * sizeof(float);
 }
 
 int wa_decode(const wa_window_t* w,
@@ -54,11 +56,11 @@ int wa_decode(const wa_window_t* w,
     if (!window_ok(w)) return WA_EARG;
     if (w->window > w->ring) return WA_ERANGE;
     if (w->window == 0 && max_pos >= w->ring) return WA_ERANGE;
-    const size_t need = wa_decode_workspace(rows, hq, d, w, max_pos);
-    if (!ws || ws_bytes < need || need == 0) return WA_EWORKSPACE;
     // 16-byte vector loads of q and K/V rows
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
     if ((q_srow | q_shead | kv_sstream | kv_sslot | kv_shead) & 7) return WA_EARG;
+    const size_t need = wa_decode_workspace(rows, hq, d, w, max_pos);
+    if (!ws || ws_bytes < need || need == 0 || ((uintptr_t)ws & 15)) return WA_EWORKSPACE;
 
     wa::DecodeArgs a{};
     a.q = q; a.q_srow = q_srow; a.q_shead = q_shead;
@@ -67,10 +69,10 @@ int wa_decode(const wa_window_t* w,
     a.max_pos = max_pos; a.rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
     a.window = w->window; a.ring = w->ring; a.scale = w->scale;
     a.C = chunk_capacity(w, max_pos);
-    const size_t cells = (size_t)rows * hq * a.C;
+    const size_t cells2 = ((size_t)rows * hq * a.C + 1) & ~(size_t)1;
     a.m = static_cast<float*>(ws);
-    a.l = a.m + cells;
-    a.o = a.l + cells;
+    a.l = a.m + cells2;
+    a.o = a.l + cells2;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
     a.rerun = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -86,6 +88,7 @@ int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* 
     if (rows <= 0 || hq <= 0 || C <= 0 || o_srow < 0 || o_shead < 0) return WA_EARG;
     if (d != 128 && d != 256) return WA_EUNSUPPORTED;
     if (!window_ok(w)) return WA_EARG;
+    if ((uintptr_t)o & 15) return WA_EARG;   // vector loads of the o partials
     wa::DecodeArgs a{};
     a.m = const_cast<float*>(m); a.l = const_cast<float*>(l); a.o = const_cast<float*>(o);
     a.pos_of_row = pos_of_row; a.rows = rows; a.hq = hq; a.hkv = hq; a.d = d; a.C = C;

@@ -59,16 +59,20 @@ def test_chunks_and_workspace():
     # 64 rows x 16 heads x 5 chunks x (m, l, 256 dims) fp32
     assert L.wa_decode_workspace(64, 16, 256, ctypes.byref(w), 0) == 64 * 16 * 5 * 258 * 4
     assert L.wa_decode_workspace(64, 16, 100, ctypes.byref(w), 0) == 0
+    # an odd cell count (7 x 3 x 3): m and l take 64 floats each so that o is 16-byte aligned
+    w300 = api.window(300, 700)
+    assert L.wa_decode_workspace(7, 3, 256, ctypes.byref(w300), 0) == (2 * 64 + 63 * 256) * 4
     bad = api.window(-1, 10)
     assert L.wa_decode_workspace(1, 1, 256, ctypes.byref(bad), 0) == 0
 
 
 def _decode(w, rows=2, hq=4, hkv=2, d=256, max_pos=100, ws_bytes=1 << 30, ptr=FAKE,
-            streams=1, strides=(1024, 256, 0, 512, 256)):
+            streams=1, strides=(1024, 256, 0, 512, 256), ws=None):
     L = api.lib()
     qs, qh, sst, ssl, sh = strides
+    ws = ptr if ws is None else ws
     return L.wa_decode(ctypes.byref(w), ptr, qs, qh, ptr, ptr, sst, ssl, sh, streams,
-                       ptr, ptr, max_pos, rows, hq, hkv, d, ptr, ws_bytes, ptr, qs, qh, None)
+                       ptr, ptr, max_pos, rows, hq, hkv, d, ws, ws_bytes, ptr, qs, qh, None)
 
 
 def test_decode_rejects_before_launch():
@@ -86,6 +90,7 @@ def test_decode_rejects_before_launch():
     assert _decode(w, ws_bytes=16) == WA_EWORKSPACE
     assert _decode(w, strides=(1024, 250, 0, 512, 256)) == WA_EARG   # 16-byte rows
     assert _decode(w, ptr=FAKE + 2) == WA_EARG                       # misaligned
+    assert _decode(w, ws=FAKE + 8) == WA_EWORKSPACE                  # workspace not 16-byte aligned
 
 
 def _prompt(w, p0=0, n=10, hq=4, hkv=2, d=256, ptr=FAKE, ws_bytes=1 << 30):
@@ -122,3 +127,4 @@ def test_merge_rejects_before_launch():
     assert L.wa_merge(ctypes.byref(w), None, FAKE, FAKE, FAKE, 1, 1, 1, 256, FAKE, 1, 1, None) == WA_EARG
     assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 96, FAKE, 1, 1, None) == WA_EUNSUPPORTED
     assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 256, FAKE, 1, 1, None) == WA_EARG
+    assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE + 8, FAKE, 1, 1, 1, 256, FAKE, 1, 1, None) == WA_EARG

@@ -89,6 +89,34 @@ def test_decode_invariants():
         assert np.array_equal(gu.run_decode(case), full)
 
 
+@pytest.mark.parametrize("rows,hq,hkv,d,win,ring,streams", [SHAPES[1], SHAPES[3], (64, 16, 8, 256, 1024, 1536, 3)])
+def test_merge_reproduces_decode(rows, hq, hkv, d, win, ring, streams):
+    """wa_merge on the partials wa_decode leaves in its workspace (layout of the header:
+    m, l, o at float offsets 0, cells, 2 cells with cells rounded up to even) gives
+    wa_decode's own bits."""
+    from sliding_window_gqa_amd import api
+    rng = np.random.default_rng(rows + 3 * d + win)
+    pos = rng.integers(0, 3001, size=rows)
+    pos[0] = 0
+    case = workloads.decode_case("merge", rows, hq, hkv, d, win, ring, streams, pos, seed=rows + d)
+    gu.log(f"merge case: {rows}x{hq}/{hkv}x{d} win{win} ring{ring}")
+    C = api.lib().wa_decode_chunks(api.window(win, ring), api.INT32_MAX)
+    need = api.decode_workspace_bytes(rows, hq, d, win, ring, api.INT32_MAX)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = api.decode(gu.dev_bf16(case.q), gu.dev_bf16(case.k), gu.dev_bf16(case.v),
+                     gu.dev_i32(case.stream), gu.dev_i32(case.pos), win, ring, case.scale,
+                     workspace=ws)
+    cells = rows * hq * C
+    cells2 = cells + (cells & 1)
+    f = ws.view(torch.float32)
+    m = f[:cells].view(rows, hq, C)
+    l_ = f[cells2:cells2 + cells].view(rows, hq, C)
+    o = f[2 * cells2:2 * cells2 + cells * d].view(rows, hq, C, d)
+    merged = api.merge(m, l_, o, gu.dev_i32(case.pos), win, ring)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_bits(merged), gu.host_bits(out))
+
+
 def test_decode_linear_cache_declared_longer():
     rows = 6
     pos = np.array([0, 100, 255, 256, 700, 999])
