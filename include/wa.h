@@ -96,7 +96,8 @@ size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_
  *   out      [rows][hq][d]          strides o_srow, o_shead
  * Device preconditions: 0 <= pos_of_row[r] <= max_pos, 0 <= stream_of_row[r] < streams, and
  * the ring holds keys [lo_r, pos_r] of row r's stream in slots j mod ring. Errors: WA_EARG,
- * WA_EUNSUPPORTED, WA_ERANGE (window > ring, or window == 0 and max_pos >= ring),
+ * WA_EUNSUPPORTED, WA_ERANGE (window > ring, window == 0 and max_pos >= ring, or a key head's
+ * ring spanning 2^31 bytes or more: (ring - 1) * kv_sslot * 2 + 2 * d >= 2^31 - 1),
  * WA_EWORKSPACE, WA_EHIP.
  */
 int wa_decode(const wa_window_t* w,

@@ -56,6 +56,7 @@ int wa_decode(const wa_window_t* w,
     if (!window_ok(w)) return WA_EARG;
     if (w->window > w->ring) return WA_ERANGE;
     if (w->window == 0 && max_pos >= w->ring) return WA_ERANGE;
+    if (!wa::decode_extent_ok(w->ring, kv_sslot, d)) return WA_ERANGE;
     // 16-byte vector loads of q and K/V rows
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
     if ((q_srow | q_shead | kv_sstream | kv_sslot | kv_shead) & 7) return WA_EARG;
@@ -76,8 +77,7 @@ int wa_decode(const wa_window_t* w,
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
     a.rerun = 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (wa::launch_decode_part(a, s) != hipSuccess) return WA_EHIP;
-    if (wa::launch_merge(a, s) != hipSuccess) return WA_EHIP;
+    if (wa::launch_decode(a, s) != hipSuccess) return WA_EHIP;
     return WA_OK;
 }
 

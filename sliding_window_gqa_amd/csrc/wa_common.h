@@ -70,6 +70,10 @@ inline int prompt_pair_chunks(int window, int n) { return (window - 1 + n) / kPr
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_decode_part(const DecodeArgs& a, hipStream_t s);
+// chunk partials + merge, or whole rows in one kernel for large batches (same bits)
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// the decode kernels address a key head's ring with 32-bit offsets: its byte span must be < 2^31
+bool decode_extent_ok(int64_t ring, int64_t kv_sslot, int d);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
 

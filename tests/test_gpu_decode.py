@@ -241,3 +241,37 @@ def test_decode_inf_at_negligible_key():
     x, S, _ = gu.oracle_decode(c)
     assert x[0, 0, 3] == np.inf and out[0, 0, 3] == 0x7F80
     assert check.accept(out, x, S, E_P).all()
+
+
+def test_decode_nonfinite_whole_rows():
+    """Non-finite plants in a batch large enough for the whole-row kernel (64 rows x 8 key
+    heads, one stream per row): NaN query, visible NaN key, +inf value, +inf and -inf in one
+    column, and +inf at a key whose float64 weight is e^-200 next to a score-200 key. Every
+    output must be in its interval, with float64's class, and each planted row must have the
+    bits it has when computed alone (chunk-partial kernel + merge)."""
+    NAN, PINF, NINF = 0x7FC0, 0x7F80, 0xFF80
+    case = workloads.decode_12b(streams=64)
+    G = case.hq // case.hkv
+    lo = lambda r: attend.key_window(int(case.pos[r]), case.win)[0]
+    slot = lambda j: j % case.ring
+    case.q[3, 5, 11] = NAN
+    case.k[9, slot(int(case.pos[9]) - 40), 1, 3] = NAN
+    case.v[14, slot(lo(14) + 7), 6, 200] = PINF
+    case.v[21, slot(int(case.pos[21])), 2, 4] = PINF
+    case.v[21, slot(int(case.pos[21]) - 1), 2, 4] = NINF
+    # row 30, key head 4: both query heads all ones; key pos-5 scores 200, key pos-6 scores 0
+    r, g = 30, 4
+    p = int(case.pos[r])
+    case.q[r, g * G:(g + 1) * G] = workloads._bf16_bits(np.full(case.d, 1.0))
+    case.k[r, slot(p - 5), g] = workloads._bf16_bits(np.full(case.d, 200.0 / case.d))
+    case.k[r, slot(p - 6), g] = workloads._bf16_bits(np.zeros(case.d))
+    case.v[r, slot(p - 6), g, 3] = PINF
+    gu.log("decode case: whole-row batch with non-finite plants")
+    out = gu.run_decode(case)
+    x, S, _ = gu.oracle_decode(case)
+    assert np.isinf(x[r, g * G, 3]) and x[r, g * G, 3] > 0
+    assert check.accept(out, x, S, E_P).all()
+    for rr in (3, 9, 14, 21, 30):
+        one = workloads.DecodeCase("alone", case.q[rr:rr + 1], case.k[rr:rr + 1], case.v[rr:rr + 1],
+                                   np.array([0], np.int32), case.pos[rr:rr + 1], case.win, case.ring)
+        assert np.array_equal(gu.run_decode(one)[0], out[rr]), rr
