@@ -41,6 +41,13 @@ def build(out=LIB, extra=(), verbose=False):
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed with status {r.returncode}")
+    # a kernel whose host stub the host pass dropped leaves an undefined symbol that only
+    # fails at load time: refuse such a library here
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if nm.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel stubs missing from the host code: " + ", ".join(missing or [nm.stderr]))
     os.replace(tmp, out)
     return out
 

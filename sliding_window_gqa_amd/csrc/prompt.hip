@@ -16,15 +16,17 @@
 //     (dims x pairs). With the transposed products every lane holds a single pair (lane % 32)
 //     in all of S, P and O, so the row max, the rescale and the sum are lane-local plus one
 //     exchange between the two lane halves;
-//   * K tiles sit in LDS as [key][dim]; V tiles are transposed on their way into LDS
-//     ([dim][key]) so both MFMA operands are 16-byte LDS reads; the tiles are double
-//     buffered, the next tile's global loads are in flight while the current tile computes,
-//     and there is one barrier per tile;
+//   * K and V tiles go from memory straight into LDS ([key][dim], 16-byte chunks swizzled),
+//     by buffer loads with a per-tile descriptor on interior tiles; K fragments are 16-byte
+//     LDS reads, V^T fragments come from the transposing LDS read (ds_read_b64_tr_b16); the
+//     tiles are double buffered, the next tile's loads are in flight while the current tile
+//     computes, and there is one barrier per tile;
 //   * the K rows of a tile are fed to the first MFMA in a permuted order so that the S^T
 //     accumulator registers of a lane are, eight at a time, exactly the B operand (P^T) the
 //     P.V MFMA needs for eight consecutive keys: no shuffles between the two products;
 //   * tiles inside every pair's window skip the mask; tiles outside a wave's key range are
-//     skipped by that wave; the O rescale is skipped when no row's maximum moved;
+//     skipped by that wave; the running maximum is lazy (it moves only when a tile's maximum
+//     exceeds it by more than 2^8 in probability), so the O rescale runs on few tiles;
 //   * the workgroup index is remapped so that each XCD (8 on MI355X, workgroups dealt out
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
 //     a key head's K/V stream in that XCD's L2.
@@ -45,6 +47,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kPairs = 32 * kWaves;   // (row, head) pairs per workgroup
 constexpr int BN = 64;                // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;          // running-max slack in log2 units (p <= 256)
 
 union Pack8 {
     bf16x8 v;
@@ -86,6 +89,12 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// 16 bytes per lane from a buffer descriptor straight into LDS (buffer_load_dwordx4 ... lds):
+// lane i's bytes land at dst + 16 i.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
+}
 
 template <int D, bool P32>
 __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(PromptArgs a, int nblk) {
@@ -213,9 +222,34 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     // fetching logical chunk p ^ swz(row) of key base + row (clamped into [kmin, kmax], so
     // every fetched key is one the ring holds; keys outside every window are masked).
     const int ld_row = lane / CPR, ld_p = lane % CPR;
+    // Interior tiles (every key inside [kmin, kmax], no ring wrap inside the tile) take the
+    // fast path: buffer loads straight into LDS from a descriptor whose base is the tile's
+    // first slot (two scalar adds per tile), with the lane offsets computed once here.
+    // Edge tiles clamp each key into [kmin, kmax] and wrap it per lane.
+    uint32_t lane_off[NQ / kWaves];
+#pragma unroll
+    for (int i = 0; i < NQ / kWaves; ++i) {
+        const int q = wave + kWaves * i;
+        const int r = RPK * q + ld_row;
+        const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
+        lane_off[i] = (uint32_t)(r * a.kv_sslot + 8 * c) * 2u;
+    }
+    const int tile_extent = (int)((uint32_t)((BN - 1) * a.kv_sslot) * 2u + 2u * D);
     auto issue_tile = [&](int tile, char* kdst, char* vdst) {
         const int base = tile * BN;
         const int sbase = base % a.ring;
+        if (base >= kmin && base + BN - 1 <= kmax && sbase + BN <= a.ring) {
+            const int64_t toff = (int64_t)sbase * a.kv_sslot;
+            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + toff), (short)0, tile_extent, 0x00020000);
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + toff), (short)0, tile_extent, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < NQ / kWaves; ++i) {
+                const int q = wave + kWaves * i;
+                buffer_to_lds16(kr, kdst + 1024 * q, lane_off[i]);
+                buffer_to_lds16(vr, vdst + 1024 * q, lane_off[i]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NQ / kWaves; ++i) {
             const int q = wave + kWaves * i;
@@ -288,7 +322,11 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 #pragma unroll
                 for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[mb][r]);
             smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-            const float m_new = fmaxf(m_run, smax * cexp);
+            // lazy maximum: m moves only when the tile's maximum exceeds it by more than
+            // kLazy (log2 units), so p <= 2^kLazy and most tiles need no rescale of O
+            const float m_cand = fmaxf(m_run, smax * cexp);
+            const bool grow = m_cand > m_run + kLazy;
+            const float m_new = grow ? m_cand : m_run;
             const float mu = (m_new == -INFINITY) ? 0.f : m_new;
             float psum = 0.f;
 #pragma unroll
@@ -299,8 +337,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
                     sacc[mb][r] = p;
                     psum += p;
                 }
-            if (__any(m_new != m_run)) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+            // O and l are still zero while m is -inf: only rows with earlier keys rescale
+            if (__any(grow && m_run != -INFINITY)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
                 l_run *= alpha;
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db)
