@@ -21,7 +21,7 @@
  *   prompt  rows p0 .. p0+n-1 of one stream, tiled online softmax on MFMA (bf16 products,
  *           fp32 accumulation), key tiles at absolute positions ("Prompt" bullet); P enters
  *           P.V as one bf16, or with p32 as bf16(P) + bf16(P - bf16(P)) ("Window.p32" bullet).
- *           Windowed prompts are also split into 256-key chunks merged in chunk order.
+ *           Windowed prompts are also split into 384-key chunks merged in chunk order.
  *           A row's bits do not depend on how the prompt is chunked.
  *
  * Conventions for every entry point:
@@ -125,7 +125,7 @@ int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* 
              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
 /* Bytes of device workspace wa_prompt needs: 0 for window == 0; otherwise fp32 partials
- * m, l [n][hq][Cp] and o [n][hq][Cp][d] with Cp = (window - 1 + n) / 256 + 2, plus 16 bytes
+ * m, l [n][hq][Cp] and o [n][hq][Cp][d] with Cp = (window - 1 + n) / 384 + 2, plus 16 bytes
  * of alignment slack. 0 on invalid arguments (and for window == 0). */
 size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t d);
 
@@ -138,7 +138,7 @@ size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t 
  *   ws       device workspace, 16-byte aligned, of ws_bytes >= wa_prompt_workspace(w, n, hq, d)
  *            (may be NULL when window == 0)
  *   out      [n][hq][d]       strides o_srow, o_shead
- * With a window (> 0) the keys of every row are split into 256-key chunks at absolute
+ * With a window (> 0) the keys of every row are split into 384-key chunks at absolute
  * positions: one tiled online softmax per chunk gives fp32 partials (m in log2 units, l, O),
  * and a merge combines a row's chunks in chunk order (the decode's split applied to the
  * prompt, so that short windowed prompts fill the GPU); window 0 runs one online softmax over

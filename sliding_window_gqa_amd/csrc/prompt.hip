@@ -136,6 +136,18 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     const int head = g * G + pair % G;
     const bool valid = row < a.n;
 
+    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7, loaded before anything else
+    // so that its latency overlaps the key-range set-up
+    Pack8 qreg[KSTEPS];
+    {
+        const uint16_t* qp = a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            if (valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+            else qreg[ks].u = make_uint4(0, 0, 0, 0);
+        }
+    }
+
     const int big = 0x7FFFFFFF;
     int lo = big, last = -1;                // empty range for padding pairs
     if (valid) {
@@ -159,7 +171,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) { kmin = min(kmin, red_i[0][w]); kmax = max(kmax, red_i[1][w]); }
     if (kmax < kmin) return;                // no valid pair in this workgroup
-    // split mode: this workgroup takes the 256-key chunk cidx of its range, at absolute
+    // split mode: this workgroup takes the key chunk cidx of its range, at absolute
     // positions, and writes per-chunk partials that a merge combines in chunk order
     const bool split = a.nchunk > 1;
     const int chunk = kmin / kPromptChunk + cidx;
@@ -169,17 +181,13 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         if (kmax < kmin) return;
     }
 
-    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7. A negative scale is carried
-    // by q's sign (exact), so the exponent factor is positive and the row maximum of the
-    // raw scores gives the maximum of the scaled ones.
-    Pack8 qreg[KSTEPS];
+    // Q^T operand (loaded at the start): a negative scale is carried by q's sign (exact), so
+    // the exponent factor is positive and the row maximum of the raw scores gives the
+    // maximum of the scaled ones.
     {
-        const uint16_t* qp = a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
         const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            if (valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-            else qreg[ks].u = make_uint4(0, 0, 0, 0);
             qreg[ks].u.x ^= flip; qreg[ks].u.y ^= flip; qreg[ks].u.z ^= flip; qreg[ks].u.w ^= flip;
         }
     }

@@ -54,13 +54,15 @@ struct PromptArgs {
     int32_t window, ring; float scale; int32_t p32;
     const int32_t* hi;
     uint16_t* out; int64_t o_srow, o_shead;
-    // key-chunk split (windowed prompts): nchunk = 256-key chunks per workgroup grid slot
+    // key-chunk split (windowed prompts): nchunk = key chunks per workgroup grid slot
     // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials
     int32_t nchunk, Cp;
     float* pm; float* pl; float* po;
 };
 
-constexpr int kPromptChunk = 256;   // prompt split: keys [256c, 256c + 255], absolute
+// prompt split: keys [384c, 384c + 383], absolute (six 64-key tiles: a 1024-key window over a
+// 512-row chunk then fills the GPU in one round of workgroups)
+constexpr int kPromptChunk = 384;
 
 // Chunk capacities of the windowed-prompt split (both are bounds, independent of the data):
 // chunks a workgroup's key range can touch, and chunks one row's key range can touch

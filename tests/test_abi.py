@@ -115,8 +115,8 @@ def test_prompt_rejects_before_launch():
 def test_prompt_workspace_sizes():
     L = api.lib()
     w = api.window(1024, 1536)
-    # 512 rows x 16 heads x ((1023 + 512) / 256 + 2 = 7 chunks) x (m, l, 256 dims) + slack
-    assert L.wa_prompt_workspace(ctypes.byref(w), 512, 16, 256) == 512 * 16 * 7 * 258 * 4 + 16
+    # 512 rows x 16 heads x ((1023 + 512) / 384 + 2 = 5 chunks) x (m, l, 256 dims) + slack
+    assert L.wa_prompt_workspace(ctypes.byref(w), 512, 16, 256) == 512 * 16 * 5 * 258 * 4 + 16
     assert L.wa_prompt_workspace(ctypes.byref(api.window(0, 4096)), 512, 16, 256) == 0
     assert L.wa_prompt_workspace(ctypes.byref(w), 512, 16, 64) == 0
 
