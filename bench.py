@@ -8,9 +8,11 @@ One step is one pass of the whole hot path of a Gemma-4-12B-shaped sliding layer
 request #1123's receipt (each row reads its visible keys' K and V: 8 MiB for a full 12B
 row), with L2/MALL flushed (by reading 512 MiB) before every timed decode call. Prefill throughput
 is reported beside it, and the long non-windowed prompt (37,810 x 56 x 128, non-causal) is
-timed on its own as the MFMA-bound shape.
+timed on its own as the MFMA-bound shape, followed by that prompt's q/k preparation
+(RMSNorm + RoPE, the HBM-bound step on the input side).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--long-iters 3] [--no-cpu]
+                    [--no-long] [--no-prep]
 
 Prints one JSON line.
 """
@@ -223,6 +225,52 @@ def cpu_baseline(case, budget_s=10.0):
                       f"(numpy float64, BLAS threads as shown)"}
 
 
+class Preparer:
+    """The long prompt's q and k preparation (contract recipe: per-head RMSNorm, RoPE on dims
+    0-95 with bf16 coefficients): 37,810 rows x 112 heads (56 q + 56 k) x 128, read from the
+    interleaved projection buffer (row stride 21,504), written as contiguous rows."""
+
+    def __init__(self):
+        n, heads, d = 37810, 56, 128
+        g = torch.Generator(device="cuda").manual_seed(1006)
+        self.buf = torch.randn((n, 3 * heads * d), generator=g, device="cuda").to(torch.bfloat16)
+        self.x = self.buf[:, 0:2 * heads * d].view(n, 2 * heads, d)
+        self.pos = torch.arange(n, dtype=torch.int32, device="cuda")
+        self.out = torch.empty((n, 2 * heads, d), dtype=torch.bfloat16, device="cuda")
+        self.p = api.Prep(api.PREP_RMS_ROPE, 96, 10000.0, api.PREP_EPS[api.PREP_RMS_ROPE])
+        x = self.x
+        self.args = (ctypes.byref(self.p), x.data_ptr(), x.stride(0), x.stride(1), self.pos.data_ptr(),
+                     None, n, 2 * heads, d, None, 0, 0, self.out.data_ptr(), 0, self.out.stride(0),
+                     self.out.stride(1), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self.bytes = 2 * n * 2 * heads * d * 2          # bf16 read + written
+        self.fn = api.lib().wa_prepare
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"wa_prepare status {st}")
+
+
+def prepare_long_leg(iters):
+    pr = Preparer()
+    pr(); torch.cuda.synchronize()
+    t = Timed()
+    for _ in range(max(iters, 3)):
+        with t:
+            pr()
+    ms = float(np.median(t.ms()))
+    gbs = pr.bytes / (ms * 1e-3) / 1e9
+    rl = roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic_bytes("prepare_long", ["prepare_kernel"]))
+    rl["kernel"] = "prepare_kernel<128> (RMSNorm + RoPE 96 dims, bf16 coefficients)"
+    out = {"prepare_long": {"workload": "q/k preparation of the long prompt: 37,810 x 112 heads x 128, "
+                                        "RMSNorm eps 1e-5 + split-half RoPE on dims 0-95, from the "
+                                        "interleaved projection buffer",
+                            "ms": round(ms, 4), "bytes_per_call": pr.bytes, "gbs": round(gbs, 2)},
+           "roofline_prepare_long": rl}
+    del pr
+    return out
+
+
 def profile_driver(names, iters):
     """Run the workloads for profiler passes, after a plain copy of known size."""
     a = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -235,7 +283,8 @@ def profile_driver(names, iters):
             "decode12b64": lambda: Decoder(workloads.decode_12b(streams=64)),
             "prompt12b": lambda: Prompter(workloads.prompt_12b()),
             "prompt31b": lambda: Prompter(workloads.prompt_31b()),
-            "long": lambda: Prompter(workloads.long_prompt())}
+            "long": lambda: Prompter(workloads.long_prompt()),
+            "prepare_long": lambda: Preparer()}
     for n in names:
         f = make[n]()
         torch.cuda.synchronize()
@@ -254,10 +303,11 @@ def main():
     ap.add_argument("--long-iters", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-prep", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiler driver: run a 256 MiB device copy (counter calibration), then "
                          "each listed workload (decode12b, decode12b64, prompt12b, prompt31b, "
-                         "long) --steps times; no timing, no JSON")
+                         "long, prepare_long) --steps times; no timing, no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -374,6 +424,9 @@ def main():
         rl["kernel"] = "prompt_kernel<128,bf16P> (long prompt)"
         res["roofline_prefill_long"] = rl
         del lp
+
+    if not args.no_long and not args.no_prep:
+        res.update(prepare_long_leg(args.long_iters))
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(dcase)

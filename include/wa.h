@@ -156,6 +156,43 @@ int wa_prompt(const wa_window_t* w,
               const int32_t* hi, void* ws, size_t ws_bytes,
               uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
+/* q/k row preparation, the step before the attention (TensorFold pull request #1257,
+ * "What this changes"; the "Exact Numerical Contract" page, "Preparation"). */
+enum {
+    WA_PREP_COPY = 0,      /* the row as it is (values into the cache) */
+    WA_PREP_ROPE_L2 = 1,   /* r = bf16(rope(x)), n = bf16(r / sqrt(sum r^2 + eps)),
+                              then q = bf16(qs * n) when qs is given (fp32 cos/sin) */
+    WA_PREP_RMS_ROPE = 2   /* n = bf16(x / sqrt(mean x^2 + eps)), r = bf16(rope(n)) with
+                              bf16 cos/sin coefficients */
+};
+typedef struct wa_prep {
+    int32_t mode;       /* WA_PREP_* */
+    int32_t rope_dims;  /* R: even, 0 <= R <= d; rotate-half over dims 0..R-1, pairs (j, j+R/2) */
+    float   theta;      /* RoPE base: inv_j = fl32(theta^(-2j/R)), angle fl32(fl32(pos) * inv_j) */
+    float   eps;        /* the pages' values: 1e-6 on the sum (L2), 1e-5 on the mean (RMS) */
+} wa_prep_t;
+
+/*
+ * Prepare rows r = 0 .. rows-1 (position pos_of_row[r], device int32) of `heads` heads:
+ *   x    [rows][heads][d] bf16, strides x_srow, x_shead (the projection's rows)
+ *   qs   fp32 [d] (device) or NULL: q scale of WA_PREP_ROPE_L2 (rejected in other modes)
+ *   out  ring == 0: row r at out + r * o_sslot (+ head * o_shead);
+ *        ring  > 0: row r into the cache slot pos mod ring of stream stream_of_row[r]:
+ *                   out + stream * o_sstream + (pos mod ring) * o_sslot + head * o_shead
+ * cos and sin are the fp32 values of the angle's cosine and sine, correctly rounded
+ * (within the page's 2-ulp cosf/sinf); all other arithmetic is fp32 and every rounding
+ * point named in the mode rounds to bf16, nearest-even.
+ * Device preconditions: pos >= 0 (negative values are taken as 0), 0 <= stream_of_row[r]
+ * < streams (clamped). x and out 8-byte aligned (4-byte at d = 128), strides multiples of 4
+ * (2 at d = 128). Errors: WA_EARG, WA_EUNSUPPORTED (d other than 128 or 256), WA_EHIP.
+ */
+int wa_prepare(const wa_prep_t* p,
+               const uint16_t* x, int64_t x_srow, int64_t x_shead,
+               const int32_t* pos_of_row, const float* qs,
+               int32_t rows, int32_t heads, int32_t d,
+               const int32_t* stream_of_row, int32_t streams, int32_t ring,
+               uint16_t* out, int64_t o_sstream, int64_t o_sslot, int64_t o_shead, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* wa_status_string(int status);
 

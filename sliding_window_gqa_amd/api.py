@@ -27,6 +27,15 @@ def window(window, ring, scale=1.0, p32=False):
     return Window(int(window), int(ring), float(scale), 1 if p32 else 0)
 
 
+class Prep(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+                ("theta", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+PREP_COPY, PREP_ROPE_L2, PREP_RMS_ROPE = 0, 1, 2
+# the pages' epsilons: on the sum of squares (L2), on their mean (RMSNorm)
+PREP_EPS = {PREP_ROPE_L2: 1e-6, PREP_RMS_ROPE: 1e-5, PREP_COPY: 0.0}
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -44,6 +53,8 @@ SIGNATURES = {
     "wa_prompt_workspace": (_SZ, [_WP, _I32, _I32, _I32]),
     "wa_prompt": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64,
                                  _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _I64, _I64, _P]),
+    "wa_prepare": (ctypes.c_int, [ctypes.POINTER(Prep), _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
+                                  _P, _I32, _I32, _P, _I64, _I64, _I64, _P]),
     "wa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "wa_version": (ctypes.c_char_p, []),
 }
@@ -167,4 +178,37 @@ def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None, work
                            k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
                            int(p0), n, hq, hkv, d, hp, wp, wn, out.data_ptr(), out.stride(0),
                            out.stride(1), _stream()))
+    return out
+
+
+def prepare(x, pos_of_row, mode, rope_dims=0, theta=10000.0, qs=None, eps=None, out=None,
+            stream_of_row=None, ring=0):
+    """q/k row preparation (wa_prepare). x [rows, heads, d] bf16 (CUDA, unit dim stride);
+    pos_of_row int32 [rows]; qs float32 [d] or None. With ring == 0 the result is a new (or
+    the given) [rows, heads, d] tensor; with ring > 0, ``out`` is the cache
+    [streams, ring, heads, d] and row r goes to slot pos mod ring of stream_of_row[r]."""
+    _bf16(x, "x"); _i32(pos_of_row, "pos_of_row")
+    rows, heads, d = x.shape
+    p = Prep(int(mode), int(rope_dims), float(theta), float(PREP_EPS[mode] if eps is None else eps))
+    qp = None
+    if qs is not None:
+        if qs.dtype != torch.float32 or not qs.is_cuda or not qs.is_contiguous() or qs.numel() != d:
+            raise TypeError("qs must be a contiguous float32 CUDA tensor of d values")
+        qp = qs.data_ptr()
+    if ring > 0:
+        if out is None or stream_of_row is None:
+            raise ValueError("a ring write needs the cache tensor and stream_of_row")
+        _bf16(out, "out"); _i32(stream_of_row, "stream_of_row")
+        if out.dim() != 4 or out.shape[1] != ring or out.shape[2] != heads or out.shape[3] != d:
+            raise ValueError("out must be [streams, ring, heads, d]")
+        streams, sst, ssl, sh = out.shape[0], out.stride(0), out.stride(1), out.stride(2)
+        sp = stream_of_row.data_ptr()
+    else:
+        if out is None:
+            out = torch.empty((rows, heads, d), dtype=torch.bfloat16, device=x.device)
+        _bf16(out, "out")
+        streams, sst, ssl, sh, sp = 0, 0, out.stride(0), out.stride(1), None
+    _check(lib().wa_prepare(ctypes.byref(p), x.data_ptr(), x.stride(0), x.stride(1),
+                            pos_of_row.data_ptr(), qp, rows, heads, d, sp, streams, int(ring),
+                            out.data_ptr(), sst, ssl, sh, _stream()))
     return out

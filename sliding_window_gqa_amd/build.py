@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwa.so")
-SOURCES = ["decode.hip", "prompt.hip", "wa_abi.hip"]
+SOURCES = ["decode.hip", "prompt.hip", "prepare.hip", "wa_abi.hip"]
 ARCH = "gfx950"
 
 

@@ -151,6 +151,40 @@ int wa_prompt(const wa_window_t* w,
     return WA_OK;
 }
 
+int wa_prepare(const wa_prep_t* p,
+               const uint16_t* x, int64_t x_srow, int64_t x_shead,
+               const int32_t* pos_of_row, const float* qs,
+               int32_t rows, int32_t heads, int32_t d,
+               const int32_t* stream_of_row, int32_t streams, int32_t ring,
+               uint16_t* out, int64_t o_sstream, int64_t o_sslot, int64_t o_shead, void* stream) {
+    if (!p || !x || !pos_of_row || !out) return WA_EARG;
+    if (rows <= 0 || heads <= 0 || x_srow < 0 || x_shead < 0 || o_sslot < 0 || o_shead < 0 ||
+        o_sstream < 0 || ring < 0)
+        return WA_EARG;
+    if (d != 128 && d != 256) return WA_EUNSUPPORTED;
+    if (p->mode != WA_PREP_COPY && p->mode != WA_PREP_ROPE_L2 && p->mode != WA_PREP_RMS_ROPE) return WA_EARG;
+    if (p->mode != WA_PREP_COPY) {
+        if (p->rope_dims < 0 || p->rope_dims > d || (p->rope_dims & 1)) return WA_EARG;
+        if (!(p->theta > 0.f) || !(p->eps >= 0.f)) return WA_EARG;
+    }
+    if (qs && p->mode != WA_PREP_ROPE_L2) return WA_EARG;
+    if (ring > 0 && (!stream_of_row || streams <= 0)) return WA_EARG;
+    // 4- or 8-byte lane accesses (d / 64 bf16 a lane)
+    const uintptr_t al = (uintptr_t)(d / 32);
+    if (((uintptr_t)x | (uintptr_t)out) & (al - 1)) return WA_EARG;
+    if ((x_srow | x_shead | o_sstream | o_sslot | o_shead) & (int64_t)(al / 2 - 1)) return WA_EARG;
+    if (qs && ((uintptr_t)qs & 3)) return WA_EARG;
+    wa::PrepArgs a{};
+    a.mode = p->mode; a.rope_dims = p->rope_dims; a.theta = p->theta; a.eps = p->eps;
+    a.x = x; a.x_srow = x_srow; a.x_shead = x_shead;
+    a.pos_of_row = pos_of_row; a.qs = qs;
+    a.rows = rows; a.heads = heads; a.d = d;
+    a.stream_of_row = stream_of_row; a.streams = streams; a.ring = ring;
+    a.out = out; a.o_sstream = o_sstream; a.o_sslot = o_sslot; a.o_shead = o_shead;
+    if (wa::launch_prepare(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
+    return WA_OK;
+}
+
 const char* wa_status_string(int status) {
     switch (status) {
         case WA_OK: return "ok";

@@ -64,6 +64,17 @@ struct PromptArgs {
 // 512-row chunk then fills the GPU in one round of workgroups)
 constexpr int kPromptChunk = 384;
 
+// q/k row preparation (modes as in wa.h)
+constexpr int kPrepCopy = 0, kPrepRopeL2 = 1, kPrepRmsRope = 2;
+struct PrepArgs {
+    int32_t mode, rope_dims; float theta, eps;
+    const uint16_t* x; int64_t x_srow, x_shead;
+    const int32_t* pos_of_row; const float* qs;
+    int32_t rows, heads, d;
+    const int32_t* stream_of_row; int32_t streams, ring;
+    uint16_t* out; int64_t o_sstream, o_sslot, o_shead;
+};
+
 // Chunk capacities of the windowed-prompt split (both are bounds, independent of the data):
 // chunks a workgroup's key range can touch, and chunks one row's key range can touch
 // (a row's last key is at most p0 + n - 1, so its range spans at most window - 1 + n keys).
@@ -78,5 +89,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 bool decode_extent_ok(int64_t ring, int64_t kv_sslot, int d);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s);
+hipError_t launch_prepare(const PrepArgs& a, hipStream_t s);
 
 }  // namespace wa

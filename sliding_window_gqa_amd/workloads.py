@@ -248,3 +248,31 @@ def long_prompt_sample_rows(n, per_head=256, seed=1005):
     rng = np.random.Generator(np.random.PCG64(seed + 104729))
     inner = rng.choice(np.arange(1, n - 1), size=min(per_head, n) - 2, replace=False)
     return np.sort(np.concatenate([[0], inner, [n - 1]])).astype(np.int64)
+
+
+@dataclass
+class PrepCase:
+    """Projection rows for the q/k preparation: x [rows, heads, d] bf16 bits at positions
+    pos [rows]; qs float32 [d] or None (the L2 recipe's q scale)."""
+    name: str
+    x: np.ndarray
+    pos: np.ndarray
+    rope_dims: int
+    theta: float = 10000.0
+    qs: Optional[np.ndarray] = None
+
+
+def prep_case(name, rows, heads, d, rope_dims, seed, pos=None, with_qs=False, theta=10000.0):
+    """Projection rows with a per-(row, head) scale drawn log-uniform in [0.25, 4] (heads of
+    very different sizes), Gaussian directions, and positions a third of which lie past
+    199,800 (TensorFold pull request #1257, "Kernel contract": a third of the rows past
+    position 199,800); the q scale, when asked, is a positive fp32 vector in [0.5, 3]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if pos is None:
+        pos = np.concatenate([rng.integers(0, 8192, rows - rows // 3),
+                              rng.integers(199_801, 262_144, rows // 3)])
+        rng.shuffle(pos)
+    scale = np.exp(rng.uniform(np.log(0.25), np.log(4.0), size=(rows, heads)))
+    x = _bf16_bits(scale[..., None] * rng.standard_normal((rows, heads, d)))
+    qs = rng.uniform(0.5, 3.0, d).astype(np.float32) if with_qs else None
+    return PrepCase(name, x, np.asarray(pos, np.int32), rope_dims, theta, qs)

@@ -128,3 +128,28 @@ def test_merge_rejects_before_launch():
     assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 96, FAKE, 1, 1, None) == WA_EUNSUPPORTED
     assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 256, FAKE, 1, 1, None) == WA_EARG
     assert L.wa_merge(ctypes.byref(w), FAKE, FAKE, FAKE + 8, FAKE, 1, 1, 1, 256, FAKE, 1, 1, None) == WA_EARG
+
+
+def _prepare(mode=1, R=256, theta=10000.0, eps=1e-6, x=FAKE, pos=FAKE, qs=None, rows=2, heads=2,
+             d=256, st=None, streams=0, ring=0, out=FAKE, o_sstream=0, o_sslot=512, o_shead=256,
+             x_srow=512, x_shead=256):
+    p = api.Prep(mode, R, theta, eps)
+    return api.lib().wa_prepare(ctypes.byref(p), x, x_srow, x_shead, pos, qs, rows, heads, d,
+                                st, streams, ring, out, o_sstream, o_sslot, o_shead, None)
+
+
+def test_prepare_rejects_before_launch():
+    assert _prepare(x=None) == WA_EARG
+    assert _prepare(pos=None) == WA_EARG
+    assert _prepare(rows=0) == WA_EARG
+    assert _prepare(d=64) == WA_EUNSUPPORTED
+    assert _prepare(mode=7) == WA_EARG
+    assert _prepare(R=257) == WA_EARG                      # odd rotated width
+    assert _prepare(R=258) == WA_EARG                      # wider than the head
+    assert _prepare(theta=0.0) == WA_EARG
+    assert _prepare(theta=float("nan")) == WA_EARG
+    assert _prepare(mode=2, qs=FAKE) == WA_EARG             # q scale belongs to the L2 recipe
+    assert _prepare(ring=16) == WA_EARG                     # ring write without streams
+    assert _prepare(x=FAKE + 4) == WA_EARG                  # 8-byte lane loads at d = 256
+    assert _prepare(x_srow=514) == WA_EARG
+    assert _prepare(ring=-1) == WA_EARG
