@@ -391,9 +391,9 @@ def main():
     rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s",
                          traffic_bytes("prompt12b", ["prompt_kernel"]))
     rl_decode = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                         traffic_bytes("decode12b", ["decode_part_kernel", "merge_kernel"]))
+                         traffic_bytes("decode12b", ["decode_kernel", "merge_kernel"]))
     rl_prompt["kernel"] = "prompt_kernel<256,p32> (12B prompt chunk)"
-    rl_decode["kernel"] = "decode_part_kernel<256,2> + merge_kernel<256> (unique K/V bytes)"
+    rl_decode["kernel"] = "decode_kernel<256,2,whole rows> (unique K/V bytes)"
     res["roofline"] = rl_prompt if pms >= dms else rl_decode
     res["roofline_decode"] = rl_decode
     hgbs = hu["row_bytes"] / (hms * 1e-3) / 1e9
@@ -401,8 +401,8 @@ def main():
                                 "ms": round(hms, 5), "bytes_per_call": hu["row_bytes"],
                                 "gbs": round(hgbs, 2)}
     rl_h = roofline("hbm", hgbs, HBM_PEAK_GBS, "GB/s",
-                    traffic_bytes("decode12b64", ["decode_part_kernel", "merge_kernel"]))
-    rl_h["kernel"] = "decode_part_kernel<256,2> + merge_kernel<256> (64 streams)"
+                    traffic_bytes("decode12b64", ["decode_kernel", "merge_kernel"]))
+    rl_h["kernel"] = "decode_kernel<256,2,whole rows> (64 streams)"
     res["roofline_decode_64_streams"] = rl_h
 
     if not args.no_long:

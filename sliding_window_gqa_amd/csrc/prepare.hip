@@ -17,8 +17,10 @@
 // computed once (float64 pow, cos and sin of the fp32 angle, each rounded once to fp32,
 // i.e. a correctly rounded cosf/sinf) into LDS and shared by all heads. Each wave takes
 // heads h = wave, wave + 4, ... and loads eight of them before computing any: a lane holds
-// D/64 consecutive dims (one 4- or 8-byte load), partners of the rotation come through
-// LDS, the sum of squares is a wave butterfly.
+// D/64 consecutive dims (one 4- or 8-byte load), the lane's cos/sin and partner index are
+// fixed for the row, partners of the rotation come through LDS (one row per batch entry,
+// so the eight heads' chains interleave), the sum of squares is a VALU-only wave sum and
+// the bf16 roundings are hardware conversions (v_cvt_pk_bf16_f32, nearest-even).
 #include "wa_common.h"
 
 namespace wa {
@@ -28,8 +30,6 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kBatch = 8;              // heads a wave loads before using any
 
-// Sum over the 64 lanes of a wave, the result in every lane, on the VALU only: DPP quad
-// permutes and row mirrors inside 16 lanes, then the 16- and 32-lane swaps.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -47,6 +47,8 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// Sum over the 64 lanes of a wave, the result in every lane, on the VALU only: DPP quad
+// permutes and row mirrors inside 16 lanes, then the 16- and 32-lane swaps.
 __device__ __forceinline__ float wave_sum64(float v) {
     v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]
