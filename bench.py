@@ -65,8 +65,8 @@ def decode_units(case):
 
 def prompt_units(case):
     """MFMA flops the method performs: 2d for S and 2d per P.V product per visible
-    (row, head, key); p32 runs P.V twice."""
-    pv = 2 if case.p32 else 1
+    (row, head, key); P.V runs once per bf16 part of P (one, two with p32, or three)."""
+    pv = 1 + api._p_mode(case.p32)
     triples = 0
     for i in range(case.n):
         last = None if case.hi is None else int(case.hi[i])
@@ -271,6 +271,11 @@ def prepare_long_leg(iters):
     return out
 
 
+def _three(case):
+    case.p32 = api.P_THREE
+    return case
+
+
 def profile_driver(names, iters):
     """Run the workloads for profiler passes, after a plain copy of known size."""
     a = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -284,6 +289,8 @@ def profile_driver(names, iters):
             "prompt12b": lambda: Prompter(workloads.prompt_12b()),
             "prompt31b": lambda: Prompter(workloads.prompt_31b()),
             "long": lambda: Prompter(workloads.long_prompt()),
+            "long3": lambda: Prompter(workloads.long_prompt(p32=api.P_THREE)),
+            "prompt12b3": lambda: Prompter(_three(workloads.prompt_12b())),
             "prepare_long": lambda: Preparer()}
     for n in names:
         f = make[n]()
@@ -306,8 +313,8 @@ def main():
     ap.add_argument("--no-prep", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiler driver: run a 256 MiB device copy (counter calibration), then "
-                         "each listed workload (decode12b, decode12b64, prompt12b, prompt31b, "
-                         "long, prepare_long) --steps times; no timing, no JSON")
+                         "each listed workload (decode12b, decode12b64, prompt12b, prompt12b3, "
+                         "prompt31b, long, long3, prepare_long) --steps times; no timing, no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -424,6 +431,45 @@ def main():
         rl["kernel"] = "prompt_kernel<128,bf16P> (long prompt)"
         res["roofline_prefill_long"] = rl
         del lp
+
+    # P as three bf16 parts (fp32-accurate P.V): the 12B prompt chunk and the long prompt
+    tcase = workloads.prompt_12b()
+    tcase.p32 = api.P_THREE
+    tp3 = Prompter(tcase)
+    tu = prompt_units(tcase)
+    for _ in range(args.warmup):
+        tp3()
+    t3 = Timed()
+    for _ in range(args.steps):
+        flush()
+        with t3:
+            tp3()
+    t3ms = float(np.mean(t3.ms()))
+    res["prefill_three_parts"] = {"workload": "12B prompt chunk with P as three bf16 parts",
+                                  "ms": round(t3ms, 5),
+                                  "tflops": round(tu["flops"] / (t3ms * 1e-3) / 1e12, 2),
+                                  "flops_per_call": tu["flops"],
+                                  "flop_accounting": "(2 + 2*3) * d per visible (row, head, key)"}
+    del tp3
+    if not args.no_long:
+        lcase3 = workloads.long_prompt(p32=api.P_THREE)
+        lp3 = Prompter(lcase3)
+        lu3 = prompt_units(lcase3)
+        lp3(); torch.cuda.synchronize()
+        tl3 = Timed()
+        for _ in range(args.long_iters):
+            with tl3:
+                lp3()
+        l3ms = float(np.mean(tl3.ms()))
+        l3tf = lu3["flops"] / (l3ms * 1e-3) / 1e12
+        res["prefill_long_three_parts"] = {"workload": "long prompt 37,810 x 56 x 128, non-causal, P as three bf16 parts",
+                                           "ms": round(l3ms, 3), "tflops": round(l3tf, 2),
+                                           "flops_per_call": lu3["flops"]}
+        rl3 = roofline("mfma", l3tf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
+                       traffic_bytes("long3", ["prompt_kernel"]))
+        rl3["kernel"] = "prompt_kernel<128,3 parts> (long prompt)"
+        res["roofline_prefill_long_three_parts"] = rl3
+        del lp3
 
     if not args.no_long and not args.no_prep:
         res.update(prepare_long_leg(args.long_iters))

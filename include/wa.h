@@ -20,7 +20,8 @@
  *           stream slot or the declared cache length.
  *   prompt  rows p0 .. p0+n-1 of one stream, tiled online softmax on MFMA (bf16 products,
  *           fp32 accumulation), key tiles at absolute positions ("Prompt" bullet); P enters
- *           P.V as one bf16, or with p32 as bf16(P) + bf16(P - bf16(P)) ("Window.p32" bullet).
+ *           P.V as one bf16, or with p32 as bf16(P) + bf16(P - bf16(P)) ("Window.p32" bullet),
+ *           or as three bf16 parts that sum to P exactly (WA_P_THREE).
  *           Windowed prompts are also split into 384-key chunks merged in chunk order.
  *           A row's bits do not depend on how the prompt is chunked.
  *
@@ -60,8 +61,19 @@ typedef struct wa_window {
     int32_t window;  /* keys a row sees up to its last key; 0 = no window (linear cache) */
     int32_t ring;    /* slots per stream in the K/V cache (the cache length when window == 0) */
     float   scale;   /* score scale: s = scale * (q . k) */
-    int32_t p32;     /* prompt only: nonzero = P as two bf16 halves, zero = P as one bf16 */
+    int32_t p32;     /* prompt only: how P enters P.V, one of WA_P_* below */
 } wa_window_t;
+
+/* Values of wa_window_t.p32 (the prompt's representation of the fp32 probabilities P in the
+ * bf16 P.V product; fp32 accumulation in every case):
+ *   WA_P_BF16   one bf16, bf16(P) (relative error up to 2^-8)               "Window.p32" off
+ *   WA_P_TWO    two parts, bf16(P) + bf16(P - bf16(P)) (P to 2^-16)           "Window.p32" on
+ *   WA_P_THREE  three parts hi + mid + lo, each the bf16 rounding of what the earlier parts
+ *               leave; their sum is P exactly (P >= 2^-110), so the P.V products are those of
+ *               fp32 P (the three-part 16-bit split of TensorFold pull request #1622, review
+ *               answer, "What changed"); P.V costs three MFMA passes.
+ * Other values: WA_EUNSUPPORTED. */
+enum { WA_P_BF16 = 0, WA_P_TWO = 1, WA_P_THREE = 2 };
 
 enum {
     WA_OK = 0,
@@ -147,6 +159,7 @@ size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t 
  * The ring must hold keys [min lo_i, p0 + n - 1] without two of them sharing a slot:
  * ring >= p0 + n - max(0, p0 - window + 1) (window > 0) or ring >= p0 + n (window == 0),
  * else WA_ERANGE. hi values out of range are clamped into [p0 + i, p0 + n - 1].
+ * w->p32 selects P's representation (WA_P_*; another value is WA_EUNSUPPORTED).
  * Errors: WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE, WA_EHIP.
  */
 int wa_prompt(const wa_window_t* w,

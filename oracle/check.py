@@ -11,9 +11,11 @@ The interval is [x - w, x + w] with half-width (two tiers):
   tier "S" (strict, used to show planted mistakes go red):  w = (e_P + 2**-16) S
 
   x    the float64 value, S = sum_j p_j |v_j| / l (>= |x|), both from ``attend``;
-  e_P  the representation error of P fed to P.V: 0 for fp32 P (decode), 2**-16 for P as
-       two bf16 halves (Window.p32 bullet: fp32's probabilities to 2**-16), 2**-8 for P as
-       one bf16 (the page's gate-4 remark gives P's own bound as 2**-8);
+  e_P  the representation error of P fed to P.V: 0 for fp32 P (decode), and for P as three
+       bf16 parts whose sum is fp32's P exactly (TensorFold pull request #1622, review
+       answer: the three-part 16-bit split; exact for P >= 2**-110), 2**-16 for P as two
+       bf16 halves (Window.p32 bullet: fp32's probabilities to 2**-16), 2**-8 for P as one
+       bf16 (the page's gate-4 remark gives P's own bound as 2**-8);
   2**-8 |x|   one bf16 ulp relative to the value;
   2**-16 S    an allowance for fp32 sums, exponentials and the score spread, which carry
               absolute error in proportion to S, not to |x|.
@@ -27,6 +29,7 @@ import numpy as np
 from . import bf16
 
 E_P_FP32 = 0.0
+E_P_THREE = 0.0
 E_P_P32 = 2.0 ** -16
 E_P_BF16 = 2.0 ** -8
 

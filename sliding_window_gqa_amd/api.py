@@ -23,8 +23,18 @@ class Window(ctypes.Structure):
                 ("scale", ctypes.c_float), ("p32", ctypes.c_int32)]
 
 
+# Window.p32 values: P enters P.V as one bf16, two bf16 parts, or three parts summing to P
+P_BF16, P_TWO, P_THREE = 0, 1, 2
+
+
+def _p_mode(p32):
+    # a bool maps onto the page's flag: False -> one bf16, True -> two parts
+    return P_BF16 if p32 is None else int(p32)
+
+
 def window(window, ring, scale=1.0, p32=False):
-    return Window(int(window), int(ring), float(scale), 1 if p32 else 0)
+    """p32: False/0 (one bf16 P), True/1 (two parts) or 2 (three parts, P exactly)."""
+    return Window(int(window), int(ring), float(scale), _p_mode(p32))
 
 
 class Prep(ctypes.Structure):

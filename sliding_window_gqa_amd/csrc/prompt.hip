@@ -4,9 +4,15 @@
 // "What this changes", Prompt, Window.p32 and promptRows(..., hi) bullets. Each row i sees
 // keys [lo_i, last_i]; keys come in tiles at absolute positions; every tile folds into the
 // running (m, l, O) of a row with one rescale; P enters P.V as one bf16 or, with p32, as
-// bf16(P) followed by bf16(P - bf16(P)). A tile that holds none of a row's keys leaves that
-// row's state exactly unchanged (alpha = 1, P = 0), so a row's bits depend only on its own
-// key range and the absolute tile grid, never on how the prompt is cut into calls.
+// bf16(P) followed by bf16(P - bf16(P)). A third mode carries P as three bf16 parts
+// (hi, mid, lo: each part the bf16 rounding of what the earlier parts leave), whose sum is
+// fp32's P exactly, so that P.V has fp32-accurate products on the bf16 matrix cores; this
+// is the three-part 16-bit split of TensorFold pull request #1622 (review answer, "What
+// changed"), applied to P. q needs no split here: it arrives as bf16, so its products with
+// k are already exact and the scale multiplies the fp32 sum.
+// A tile that holds none of a row's keys leaves that row's state exactly unchanged
+// (alpha = 1, P = 0), so a row's bits depend only on its own key range and the absolute
+// tile grid, never on how the prompt is cut into calls.
 //
 // gfx950 design (own, not the page's tensor-core layout):
 //   * a workgroup holds 4 waves; each wave owns 32 (row, query head) pairs of one key head,
@@ -96,7 +102,7 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, voi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
 }
 
-template <int D, bool P32>
+template <int D, int NP>
 __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(PromptArgs a, int nblk) {
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
@@ -361,12 +367,18 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int mb = s >> 1, r0 = (s & 1) * 8;
-                Pack8 phi, plo;
+                // NP bf16 parts of P: part k is the bf16 rounding of P minus parts 0..k-1 (each
+                // difference exact in fp32)
+                Pack8 phi, pmid, plo;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float p0 = sacc[mb][r0 + 2 * u], p1 = sacc[mb][r0 + 2 * u + 1];
                     phi.w[u] = cvt_pk_bf16(p0, p1);
-                    if (P32) plo.w[u] = cvt_pk_bf16(p0 - lo_bf16(phi.w[u]), p1 - hi_bf16(phi.w[u]));
+                    if (NP >= 2) {
+                        const float e0 = p0 - lo_bf16(phi.w[u]), e1 = p1 - hi_bf16(phi.w[u]);
+                        pmid.w[u] = cvt_pk_bf16(e0, e1);
+                        if (NP == 3) plo.w[u] = cvt_pk_bf16(e0 - lo_bf16(pmid.w[u]), e1 - hi_bf16(pmid.w[u]));
+                    }
                 }
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db) {
@@ -380,7 +392,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
                     av.w[2] = __builtin_bit_cast(uint2, x1).x;
                     av.w[3] = __builtin_bit_cast(uint2, x1).y;
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
-                    if (P32)
+                    if (NP >= 2)
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
+                    if (NP == 3)
                         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
                 }
             }
@@ -601,8 +615,9 @@ hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPairs - 1) / kPairs);
     dim3 grid(nblk * a.hkv * a.nchunk);
-    if (a.p32) hipLaunchKernelGGL((prompt_kernel<D, true>), grid, dim3(kThreads), 0, s, a, nblk);
-    else hipLaunchKernelGGL((prompt_kernel<D, false>), grid, dim3(kThreads), 0, s, a, nblk);
+    if (a.p_parts == 3) hipLaunchKernelGGL((prompt_kernel<D, 3>), grid, dim3(kThreads), 0, s, a, nblk);
+    else if (a.p_parts == 2) hipLaunchKernelGGL((prompt_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, nblk);
+    else hipLaunchKernelGGL((prompt_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t npairs = (int64_t)a.n * a.hq;

@@ -119,6 +119,7 @@ int wa_prompt(const wa_window_t* w,
         return WA_EARG;
     if (!head_shape_ok(hq, hkv, d)) return WA_EUNSUPPORTED;
     if (!window_ok(w)) return WA_EARG;
+    if (w->p32 != WA_P_BF16 && w->p32 != WA_P_TWO && w->p32 != WA_P_THREE) return WA_EUNSUPPORTED;
     if ((int64_t)p0 + n > 0x7FFFFFFF || (int64_t)n + w->window > 0x3FFFFFFF) return WA_ERANGE;
     const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
     if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
@@ -130,7 +131,7 @@ int wa_prompt(const wa_window_t* w,
     a.q = q; a.q_srow = q_srow; a.q_shead = q_shead;
     a.k = k; a.v = v; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
     a.p0 = p0; a.n = n; a.hq = hq; a.hkv = hkv; a.d = d;
-    a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p32 = w->p32 != 0;
+    a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p_parts = 1 + w->p32;
     a.hi = hi;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
     a.nchunk = 1; a.Cp = 0; a.pm = a.pl = a.po = nullptr;

@@ -51,7 +51,8 @@ struct PromptArgs {
     const uint16_t* q; int64_t q_srow, q_shead;
     const uint16_t* k; const uint16_t* v; int64_t kv_sslot, kv_shead;
     int32_t p0, n, hq, hkv, d;
-    int32_t window, ring; float scale; int32_t p32;
+    int32_t window, ring; float scale;
+    int32_t p_parts;              // bf16 parts carrying P into P.V: 1, 2 (p32) or 3
     const int32_t* hi;
     uint16_t* out; int64_t o_srow, o_shead;
     // key-chunk split (windowed prompts): nchunk = key chunks per workgroup grid slot

@@ -110,6 +110,9 @@ def test_prompt_rejects_before_launch():
     assert _prompt(api.window(0, 100), p0=50, n=51) == WA_ERANGE
     assert _prompt(w, ptr=FAKE + 8) == WA_EARG
     assert _prompt(w, ws_bytes=64) == WA_EWORKSPACE             # windowed: chunk partials
+    # P's representation: one bf16, two or three parts; nothing else
+    assert _prompt(api.window(1024, 1536, p32=3)) == WA_EUNSUPPORTED
+    assert _prompt(api.window(1024, 1536, p32=-1)) == WA_EUNSUPPORTED
 
 
 def test_prompt_workspace_sizes():

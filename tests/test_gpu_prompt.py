@@ -1,7 +1,8 @@
 """GPU parity of the MFMA prompt kernel (wa_prompt) against the float64 oracle.
 
-Gate: every bf16 output inside its tier-G interval (oracle.check) with e_P = 2**-16 for p32
-and 2**-8 for P as one bf16. Masks are pinned by peaked-edge probes; chunk invariance
+Gate: every bf16 output inside its tier-G interval (oracle.check) with e_P = 2**-16 for p32,
+2**-8 for P as one bf16 and 0 for P as three bf16 parts (which must also meet the strict
+interval of fp32 P). Masks are pinned by peaked-edge probes; chunk invariance
 (TensorFold pull request #1123, "Receipt", exactness bullet: a prompt chunk split in two
 gives every row's bits) and repeatability by byte equality.
 """
@@ -17,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 
 def e_p(p32):
-    return check.E_P_P32 if p32 else check.E_P_BF16
+    """Representation error of P: p32 False/0 one bf16, True/1 two parts, 2 three parts."""
+    return {0: check.E_P_BF16, 1: check.E_P_P32, 2: check.E_P_THREE}[int(p32)]
 
 
 def _gate(case, label, p32=None, rows=None):
@@ -45,6 +47,52 @@ def test_long_prompt_sampled():
     case = workloads.long_prompt()
     rows = workloads.long_prompt_sample_rows(case.n)
     _gate(case, "long prompt 37810x56x128 sampled", rows=rows)
+
+
+THREE = 2      # Window.p32 value: P as three bf16 parts
+
+
+def _gate_strict(case, label, rows=None):
+    """Three parts carry fp32's P exactly: tier G and the strict interval of fp32 P."""
+    out, rep = _gate(case, label, p32=THREE, rows=rows)
+    assert rep["tier_S_fail"] == 0, rep
+    return out
+
+
+def test_prompt_12b_three_parts():
+    _gate_strict(workloads.prompt_12b(), "12B prompt, P in three parts, image rows")
+
+
+def test_prompt_31b_three_parts():
+    _gate_strict(workloads.prompt_31b(), "31B prompt, P in three parts")
+
+
+def test_long_prompt_small_three_parts():
+    _gate_strict(workloads.long_prompt(n=3001, heads=4), "long prompt 3001x4x128, P in three parts")
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,p0,win,ring,span", [
+    (7, 3, 1, 256, 40, 16, 64, None),
+    (129, 16, 2, 128, 77, 100, 300, (0, 128)),
+    (200, 8, 8, 128, 1000, 0, 1200, None),
+    (300, 32, 16, 256, 1300, 1024, 1536, (10, 90)),
+])
+def test_three_parts_shapes(n, hq, hkv, d, p0, win, ring, span):
+    hi = None
+    if span is not None:
+        hi = p0 + np.arange(n)
+        a, b = span
+        hi[a:b + 1] = p0 + b
+    case = workloads.prompt_case("three parts", n, hq, hkv, d, p0, win, ring, seed=7 * n + d,
+                                 hi=hi, peak_every=3)
+    _gate_strict(case, f"three parts n{n} {hq}/{hkv}x{d} p0={p0} win{win} ring{ring}")
+
+
+def test_three_parts_chunk_invariance_and_repeat():
+    case = workloads.prompt_case("12B shape, three parts", 512, 16, 8, 256, 5000, 1024, 1536,
+                                 seed=1003, p32=THREE)
+    full = _split_check(case, (1, 255, 256, 257, 300))
+    assert np.array_equal(gu.run_prompt(case), full)
 
 
 def test_long_prompt_small_p32():
@@ -106,7 +154,7 @@ def test_prompt_mask_edges_bit_exact():
     rng = np.random.default_rng(5)
     hi = p0 + np.arange(n)
     hi[10:41] = p0 + 40
-    for p32 in (True, False):
+    for p32 in (True, False, THREE):
         for which in ("lo", "last", "lo-1", "last+1"):
             case = workloads.prompt_case("edges", n, 1, 1, d, p0, win, ring, seed=8, hi=hi,
                                          p32=p32, peak_every=0)
@@ -140,7 +188,7 @@ def test_prompt_integer_sums():
     """Every key alike: weights exactly 1 (exact in one bf16 too), integer values; the
     output is the exact mean."""
     n, p0, win, ring, d = 64, 2000, 1024, 1536, 256
-    for p32 in (True, False):
+    for p32 in (True, False, THREE):
         case = workloads.prompt_case("sums", n, 2, 1, d, p0, win, ring, seed=6, p32=p32,
                                      peak_every=0)
         case.k[:] = case.k[0, 0]
@@ -189,7 +237,7 @@ def test_prompt_nonfinite_key_and_column():
     assert check.accept(out, x, S, e_p(False)).all()
 
 
-@pytest.mark.parametrize("win,p32", [(64, False), (64, True), (0, False)])
+@pytest.mark.parametrize("win,p32", [(64, False), (64, True), (0, False), (64, 2), (0, 2)])
 def test_prompt_inf_value_unseen_by_tile_neighbours(win, p32):
     """Rows that do not see an infinite value but share its key tile get 0 * inf in the MFMA
     P.V product; their float64 re-run gives float64's finite result, and the rows that do

@@ -7,7 +7,10 @@
   float32 emulation of chunked decode with an ordered merge passes the strict tier, while
   the same emulation with one planted mistake (window one key early, merge without
   exp(m_c - M), merge rounding toward zero, P rounded to one bf16 under the p32 interval)
-  fails it. The emulation is CPU test code built from numpy float32 steps.
+  fails it; P as three bf16 parts passes the strict interval of fp32 P. The emulation is
+  CPU test code built from numpy float32 steps.
+* the three-part split (TensorFold pull request #1622, review answer): nearest-even bf16
+  parts of fp32 values sum back exactly down to 2**-110, checked with torch's conversion.
 """
 
 import numpy as np
@@ -117,25 +120,86 @@ def test_planted_mistakes_go_red(small_decode, kw):
     assert _strict_fails(c, out) > 0
 
 
-def test_one_bf16_p_goes_red_under_the_p32_interval():
+def _f(a):
+    return (np.asarray(a).astype(np.uint32) << 16).view(np.float32)
+
+
+def _bf(a):
+    """float32 -> float32 value of its bf16 rounding (torch's nearest-even conversion)."""
+    return _f(workloads._bf16_bits(np.asarray(a, dtype=np.float32)))
+
+
+def _p_parts(p, parts):
+    """fp32 P as `parts` bf16 parts: each the rounding of what the earlier parts leave."""
+    out, rest = [], p.astype(np.float32)
+    for _ in range(parts):
+        b_ = _bf(rest)
+        out.append(b_)
+        rest = (rest - b_).astype(np.float32)
+    return out
+
+
+def _emulate_prompt(case, parts):
+    """float32 emulation of a prompt with P fed to P.V as `parts` bf16 parts (products of
+    the parts with v summed in float64, as exact MFMA products with fp32-accurate sums)."""
+    out = np.empty_like(case.q)
+    for i in range(case.n):
+        lo, last = attend.key_window(case.p0 + i, case.win)
+        keys = np.arange(lo, last + 1) % case.ring
+        for h in range(case.hq):
+            K, V = _f(case.k[keys, 0]), _f(case.v[keys, 0])
+            s = (K @ _f(case.q[i, h])).astype(np.float32)
+            p = np.exp(s - s.max()).astype(np.float32)
+            pp = sum(x.astype(np.float64) for x in _p_parts(p, parts))
+            y = ((pp @ V.astype(np.float64)).astype(np.float32) / p.sum(dtype=np.float32)).astype(np.float32)
+            out[i, h] = workloads._bf16_bits(y)
+    return out
+
+
+@pytest.fixture(scope="module")
+def p_control():
     case = workloads.prompt_case("p32 control", 24, 2, 1, 256, 40, 64, 128, seed=12)
     x, S, _ = attend.prompt(case.q, case.k, case.v, case.p0, case.win, case.ring, 1.0)
-    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
-    outs = {}
-    for mode in ("p32", "bf16"):
-        out = np.empty_like(case.q)
-        for i in range(case.n):
-            lo, last = attend.key_window(case.p0 + i, case.win)
-            keys = np.arange(lo, last + 1) % case.ring
-            for h in range(case.hq):
-                K, V = f(case.k[keys, 0]), f(case.v[keys, 0])
-                s = (K @ f(case.q[i, h])).astype(np.float32)
-                p = np.exp(s - s.max()).astype(np.float32)
-                hi = f(workloads._bf16_bits(p))
-                lo_ = f(workloads._bf16_bits(p - hi))
-                pp = hi + lo_ if mode == "p32" else hi
-                y = ((pp @ V) / p.sum(dtype=np.float32)).astype(np.float32)
-                out[i, h] = workloads._bf16_bits(y)
-        outs[mode] = int((~check.accept(out, x, S, check.E_P_P32, "S")).sum())
-    assert outs["p32"] == 0
-    assert outs["bf16"] > 0
+    return case, x, S
+
+
+def test_one_bf16_p_goes_red_under_the_p32_interval(p_control):
+    case, x, S = p_control
+    fails = {n: int((~check.accept(_emulate_prompt(case, n), x, S, check.E_P_P32, "S")).sum())
+             for n in (1, 2)}
+    assert fails[2] == 0
+    assert fails[1] > 0
+
+
+def test_three_part_p_passes_the_fp32_interval(p_control):
+    # three parts carry fp32's P exactly: the strict interval of fp32 P (e_P = 0) holds
+    case, x, S = p_control
+    out = _emulate_prompt(case, 3)
+    assert int((~check.accept(out, x, S, check.E_P_THREE, "S")).sum()) == 0
+
+
+def test_three_part_split_is_exact_down_to_2_pow_minus_110():
+    # P = m 2^(e-23) with a 24-bit m: three nearest-even bf16 parts (8 significant bits
+    # each) hold all 24 bits as long as the last part's lowest bit, 2^(e-23), is at least
+    # bf16's smallest subnormal 2^-133, i.e. e >= -110. Above P's range in the kernels
+    # (P <= 2^8) nothing changes.
+    rng = np.random.default_rng(5)
+    e = rng.integers(-110, 9, 200_000)
+    m = rng.integers(2 ** 23, 2 ** 24, 200_000)
+    edge = np.array([2 ** 23, 2 ** 24 - 1, 2 ** 23 + 2 ** 15, 2 ** 23 + 2 ** 15 + 2 ** 7, 2 ** 24 - 2 ** 8 - 1])
+    e = np.concatenate([e, np.full(edge.size, -110), np.full(edge.size, 8)])
+    m = np.concatenate([m, edge, edge])
+    p = (m.astype(np.float64) * 2.0 ** (e - 23)).astype(np.float32)
+    hi, mid, lo = _p_parts(p, 3)
+    assert np.array_equal(hi.astype(np.float64) + mid + lo, p.astype(np.float64))
+    # two parts leave up to 2^-16 relative (the p32 bound), one part 2^-8 (half a bf16 ulp
+    # at the bottom of a binade)
+    two = hi.astype(np.float64) + mid
+    rel2 = np.abs(two - p) / p
+    assert rel2.max() <= 2.0 ** -16 and rel2.max() > 2.0 ** -18
+    rel1 = np.abs(hi.astype(np.float64) - p) / p
+    assert rel1.max() <= 2.0 ** -8 and rel1.max() > 2.0 ** -9
+    # below 2^-110 the last part loses bits
+    q = (m[:1000].astype(np.float64) * 2.0 ** (-112 - 23)).astype(np.float32)
+    h3 = _p_parts(q, 3)
+    assert not np.array_equal(h3[0].astype(np.float64) + h3[1] + h3[2], q.astype(np.float64))
