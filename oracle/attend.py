@@ -20,6 +20,14 @@ Readings taken where the page is silent (each also listed in the design doc):
   * keys outside the window are excluded from every sum (never multiplied by zero);
   * sums start at +0.0, so a column of signed zeros gives +0.
 
+Block-sparse prompts (TensorFold pull request #1622, "What this changes": per-row block
+masks over the union of a row group's selected blocks, causal ends, the parts/merge layout)
+narrow a prompt row's keys further: with a mask, row i sees only the keys of [lo_i, last_i]
+whose block is selected. Readings: a block is 64 consecutive keys at absolute positions
+(block b = keys 64b .. 64b + 63; the page does not give the size); the mask of a row is
+32-bit words, bit b % 32 of word b // 32 for block b, and blocks past the last word are not
+selected; a row that sees no key at all has no softmax and its output is NaN (0 / 0).
+
 Everything here is float64 with one rounding, to bf16 at the output (``bf16.to_bf16_bits``).
 Alongside the value x the oracle records S = sum_j p_j |v_j| / l, the conditioning scale the
 acceptance interval uses (S >= |x|).
@@ -34,6 +42,24 @@ def key_window(pos, win, last=None):
     """First and last visible key of a row at position ``pos`` (window ``win``, 0 = none)."""
     lo = max(0, int(pos) - int(win) + 1) if win > 0 else 0
     return lo, int(pos) if last is None else int(last)
+
+
+SPARSE_BLOCK = 64
+
+
+def visible_keys(pos, win, last=None, mask=None, block=SPARSE_BLOCK):
+    """Sorted absolute positions of the keys a row sees: [lo, last] of ``key_window``, and,
+    with a block mask (uint32 words), only those whose block's bit is set."""
+    lo, hi = key_window(pos, win, last)
+    keys = np.arange(lo, hi + 1, dtype=np.int64)
+    if mask is None:
+        return keys
+    mask = np.asarray(mask, dtype=np.uint32)
+    b = keys // block
+    word = b // 32
+    inside = word < mask.size
+    bits = (mask[np.minimum(word, max(mask.size - 1, 0))] >> (b % 32).astype(np.uint32)) & 1
+    return keys[inside & (bits == 1)]
 
 
 def chunk_range(pos, win, last=None, chunk=256):
@@ -69,7 +95,7 @@ def _head_group(qg, K, V, c):
 
 
 def attention(q, k_cache, v_cache, stream_of_row, pos_of_row, win, ring, scale,
-              last_of_row=None, rows=None):
+              last_of_row=None, rows=None, masks=None):
     """Float64 windowed GQA attention for the rows ``rows`` (default: all).
 
     q        uint16 bf16 bits [R, Hq, d]
@@ -77,6 +103,7 @@ def attention(q, k_cache, v_cache, stream_of_row, pos_of_row, win, ring, scale,
     stream_of_row, pos_of_row   int [R]
     last_of_row  int [R] or None (None: each row's last key is its own position)
     win      window (0 = none); ring: slots per stream; scale: float32 score scale
+    masks    uint32 [R, W] block masks (``visible_keys``) or None (every key of the range)
 
     Returns (x, S, out): x and S float64 [len(rows), Hq, d], out uint16 bf16 bits of x.
     """
@@ -93,12 +120,16 @@ def attention(q, k_cache, v_cache, stream_of_row, pos_of_row, win, ring, scale,
     groups = {}
     for n, i in enumerate(rows):
         last = None if last_of_row is None else last_of_row[i]
-        lo, hi = key_window(pos_of_row[i], win, last)
-        groups.setdefault((int(stream_of_row[i]), lo, hi), []).append((n, int(i)))
-    for (t, lo, hi), members in groups.items():
-        slots = np.arange(lo, hi + 1, dtype=np.int64) % ring
+        keys = visible_keys(pos_of_row[i], win, last, None if masks is None else masks[i])
+        groups.setdefault((int(stream_of_row[i]), keys.tobytes()), (keys, []))[1].append((n, int(i)))
+    for (t, _), (keys, members) in groups.items():
+        slots = keys % ring
         ns = [m[0] for m in members]
         idx = [m[1] for m in members]
+        if keys.size == 0:                         # no key: 0 / 0
+            x[ns] = np.nan
+            S[ns] = 0.0
+            continue
         for g in range(Hkv):
             K = bf16.to_f64(k_cache[t, slots, g, :])
             V = bf16.to_f64(v_cache[t, slots, g, :])
@@ -125,3 +156,13 @@ def prompt(q, k_ring, v_ring, p0, win, ring, scale, hi=None, rows=None):
     pos = p0 + np.arange(n, dtype=np.int64)
     return attention(q, k_ring[None], v_ring[None], np.zeros(n, dtype=np.int64), pos,
                      win, ring, scale, None if hi is None else np.asarray(hi), rows)
+
+
+def sparse_prompt(q, k_ring, v_ring, p0, win, ring, scale, masks, hi=None, rows=None):
+    """Block-sparse prompt: row i at position p0 + i sees the keys of its range [lo_i, last_i]
+    whose 64-key block is selected in masks[i] (uint32 words, bit b % 32 of word b // 32)."""
+    n = q.shape[0]
+    pos = p0 + np.arange(n, dtype=np.int64)
+    return attention(q, k_ring[None], v_ring[None], np.zeros(n, dtype=np.int64), pos,
+                     win, ring, scale, None if hi is None else np.asarray(hi), rows,
+                     np.asarray(masks, dtype=np.uint32))

@@ -87,6 +87,7 @@ class PromptCase:
     seed: int = 0
     buffer: Optional[np.ndarray] = None  # the interleaved buffer q/k/v view, if any
     peaks: list = field(default_factory=list)
+    masks: Optional[np.ndarray] = None   # uint32 [n, words] block masks (sparse prompts)
 
     @property
     def n(self):
@@ -241,6 +242,50 @@ def long_prompt(seed=1005, n=37810, heads=56, d=128, p32=False, block=1024):
     scale = float(np.float32(1.0 / np.sqrt(d)))
     return PromptCase(f"long non-windowed prompt {n}x{heads}x{d} non-causal", q, k, v, 0, 0, n,
                       hi, scale, p32, seed, buf, [])
+
+
+SPARSE_BLOCK = 64      # keys per selectable block of a sparse prompt
+
+
+def block_masks(rng, n, p0, nsel, words=None, block=SPARSE_BLOCK):
+    """uint32 [n, words] masks: row i (position p0 + i) selects its own block and up to
+    nsel - 1 other blocks drawn without replacement from the blocks before it (bit b % 32 of
+    word b // 32 for block b)."""
+    own = (p0 + np.arange(n)) // block
+    words = int(own.max()) // 32 + 1 if words is None else words
+    m = np.zeros((n, words), dtype=np.uint32)
+    for i in range(n):
+        b = int(own[i])
+        others = rng.choice(b, size=min(nsel - 1, b), replace=False) if b > 0 else np.zeros(0, int)
+        for x in [b, *others.tolist()]:
+            m[i, x // 32] |= np.uint32(1) << np.uint32(x % 32)
+    return m
+
+
+def sparse_prompt_case(name, n, hq, hkv, d, p0, nsel, seed, win=0, p32=2, peak_every=8):
+    """Block-sparse prompt over a linear cache holding keys 0 .. p0 + n - 1: each row selects
+    ``nsel`` 64-key blocks (its own and nsel - 1 earlier ones), causal ends, the receipt's
+    distributions; peaked keys are planted in selected blocks."""
+    ring = p0 + n
+    case = prompt_case(name, n, hq, hkv, d, p0, win, ring, seed, p32=p32, peak_every=0)
+    rng = np.random.Generator(np.random.PCG64(seed + 15485863))
+    case.masks = block_masks(rng, n, p0, nsel)
+    if peak_every:
+        def sel_range(i):
+            own = (p0 + i) // SPARSE_BLOCK
+            return own * SPARSE_BLOCK, p0 + i       # the own block's visible keys
+        case.peaks = _plant_peaks(rng, case.q, case.k[None], range(n), sel_range,
+                                  np.zeros(n, dtype=np.int32), ring, peak_every)
+    return case
+
+
+def sparse_prompt(seed=1007):
+    """The sparse prompt slice of TensorFold pull request #1622's receipts: 64 rows of a
+    7,900-token prompt (p0 7,836), 24 query heads over 2 key heads, d 256, 32 selected
+    64-key blocks a row (2,048 keys; the own block is cut at the row's position), causal,
+    P as three bf16 parts (the page's fp32 tile)."""
+    return sparse_prompt_case("sparse prompt 64 rows p0=7836 (24/2)x256 32 blocks of 64",
+                              64, 24, 2, 256, 7836, 32, seed)
 
 
 def long_prompt_sample_rows(n, per_head=256, seed=1005):
