@@ -78,6 +78,49 @@ def prompt_units(case):
     return {"triples": triples, "flops": flops, "bytes": byts}
 
 
+def sparse_units(case):
+    """MFMA flops of a block-sparse prompt: (2 + 2 * parts) * d per visible (row, head, key),
+    visible = the selected blocks' keys inside the row's range."""
+    pv = 1 + api._p_mode(case.p32)
+    triples = 0
+    for i in range(case.n):
+        last = None if case.hi is None else int(case.hi[i])
+        lo, hi = key_span(case.p0 + i, case.win, last)
+        keys = np.arange(lo, hi + 1)
+        blk = keys // workloads.SPARSE_BLOCK
+        words = case.masks[i][np.minimum(blk // 32, case.masks.shape[1] - 1)]
+        sel = (blk // 32 < case.masks.shape[1]) & (((words >> (blk % 32)) & 1) == 1)
+        triples += int(sel.sum())
+    triples *= case.hq
+    return {"triples": triples, "flops": triples * (2 + 2 * pv) * case.d}
+
+
+class SparsePrompter:
+    def __init__(self, case):
+        self.c = case
+        self.q, self.k, self.v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+        self.m = torch.from_numpy(np.ascontiguousarray(case.masks).view(np.int32)).cuda()
+        self.out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
+        api.prompt_sparse(self.q, self.k, self.v, case.p0, case.win, case.ring, self.m, case.scale,
+                          p32=case.p32, out=self.out)
+        torch.cuda.synchronize()
+        self.w = api.window(case.win, case.ring, case.scale, case.p32)
+        need = api.lib().wa_prompt_sparse_workspace(ctypes.byref(self.w), case.p0, case.n, case.hq, case.d)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        q, k = self.q, self.k
+        self.args = (ctypes.byref(self.w), q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(),
+                     self.v.data_ptr(), k.stride(0), k.stride(1), case.p0, case.n, case.hq,
+                     case.hkv, case.d, None, self.m.data_ptr(), self.m.stride(0), self.m.shape[1],
+                     self.ws.data_ptr(), self.ws.numel(), self.out.data_ptr(), self.out.stride(0),
+                     self.out.stride(1), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self.fn = api.lib().wa_prompt_sparse
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"wa_prompt_sparse status {st}")
+
+
 def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -291,6 +334,7 @@ def profile_driver(names, iters):
             "long": lambda: Prompter(workloads.long_prompt()),
             "long3": lambda: Prompter(workloads.long_prompt(p32=api.P_THREE)),
             "prompt12b3": lambda: Prompter(_three(workloads.prompt_12b())),
+            "sparse": lambda: SparsePrompter(workloads.sparse_prompt()),
             "prepare_long": lambda: Preparer()}
     for n in names:
         f = make[n]()
@@ -314,7 +358,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="profiler driver: run a 256 MiB device copy (counter calibration), then "
                          "each listed workload (decode12b, decode12b64, prompt12b, prompt12b3, "
-                         "prompt31b, long, long3, prepare_long) --steps times; no timing, no JSON")
+                         "prompt31b, sparse, long, long3, prepare_long) --steps times; no timing, "
+                         "no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -470,6 +515,31 @@ def main():
         rl3["kernel"] = "prompt_kernel<128,3 parts> (long prompt)"
         res["roofline_prefill_long_three_parts"] = rl3
         del lp3
+
+    # block-sparse prompt slice: 64 rows of a 7,900-token prompt, 32 selected 64-key blocks a
+    # row, 24/2 heads x 256, P as three parts
+    scase = workloads.sparse_prompt()
+    sp = SparsePrompter(scase)
+    su = sparse_units(scase)
+    for _ in range(args.warmup):
+        sp()
+    tsp = Timed()
+    for _ in range(args.steps):
+        flush()
+        with tsp:
+            sp()
+    sms = float(np.mean(tsp.ms()))
+    stf = su["flops"] / (sms * 1e-3) / 1e12
+    res["prefill_sparse"] = {"workload": "block-sparse prompt slice: 64 rows at p0 7,836, 24/2 x 256, "
+                                         "32 selected 64-key blocks a row, causal, P as three parts",
+                             "ms": round(sms, 5), "tflops": round(stf, 2), "triples": su["triples"],
+                             "flops_per_call": su["flops"],
+                             "flop_accounting": "(2 + 2*3) * d per selected visible (row, head, key)"}
+    rls = roofline("mfma", stf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
+                   traffic_bytes("sparse", ["prompt_kernel", "prompt_merge_kernel"]))
+    rls["kernel"] = "prompt_kernel<256,3 parts> sparse + prompt_merge_kernel"
+    res["roofline_prefill_sparse"] = rls
+    del sp
 
     if not args.no_long and not args.no_prep:
         res.update(prepare_long_leg(args.long_iters))

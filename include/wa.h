@@ -169,6 +169,34 @@ int wa_prompt(const wa_window_t* w,
               const int32_t* hi, void* ws, size_t ws_bytes,
               uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
+/* Bytes of device workspace wa_prompt_sparse needs: fp32 partials m, l [n][hq][Cs] and
+ * o [n][hq][Cs][d], Cs = (window - 1 + n) / 384 + 2 with a window, (p0 + n - 1) / 384 + 1
+ * without, plus 16 bytes of alignment slack. 0 on invalid arguments. */
+size_t wa_prompt_sparse_workspace(const wa_window_t* w, int32_t p0, int32_t n, int32_t hq, int32_t d);
+
+/*
+ * Block-sparse prompt (TensorFold pull request #1622, "What this changes": per-row block
+ * masks over the union of a row group's selected blocks, causal ends, fp32 online softmax,
+ * the parts/merge layout). Row i sees the keys j of its wa_prompt range [lo_i, last_i]
+ * whose 64-key block b = j / 64 is selected: bit b % 32 of blocks[i * blocks_srow + b / 32]
+ * (device uint32, 4-byte aligned; words at or past blocks_words count as zero). Everything
+ * else is wa_prompt's: arguments, ring rule, hi, w->p32 (WA_P_*), and the 384-key chunks at
+ * absolute positions merged in chunk order, where a chunk holding none of a row's keys takes
+ * no part. A workgroup of rows walks the union of their selected tiles; each row masks the
+ * blocks it did not select, so its bits depend only on its own keys (equal to wa_prompt's
+ * with every block selected and a window > 0). A row that sees no key gets NaN (0 / 0).
+ * Errors: WA_EARG (also blocks NULL, blocks_words <= 0, blocks_srow < blocks_words),
+ * WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE (ws smaller than wa_prompt_sparse_workspace),
+ * WA_EHIP.
+ */
+int wa_prompt_sparse(const wa_window_t* w,
+                     const uint16_t* q, int64_t q_srow, int64_t q_shead,
+                     const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
+                     int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
+                     const int32_t* hi, const uint32_t* blocks, int64_t blocks_srow,
+                     int32_t blocks_words, void* ws, size_t ws_bytes,
+                     uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
+
 /* q/k row preparation, the step before the attention (TensorFold pull request #1257,
  * "What this changes"; the "Exact Numerical Contract" page, "Preparation"). */
 enum {

@@ -63,6 +63,10 @@ SIGNATURES = {
     "wa_prompt_workspace": (_SZ, [_WP, _I32, _I32, _I32]),
     "wa_prompt": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64,
                                  _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P, _I64, _I64, _P]),
+    "wa_prompt_sparse_workspace": (_SZ, [_WP, _I32, _I32, _I32, _I32]),
+    "wa_prompt_sparse": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64,
+                                        _I32, _I32, _I32, _I32, _I32, _P, _P, _I64, _I32,
+                                        _P, _SZ, _P, _I64, _I64, _P]),
     "wa_prepare": (ctypes.c_int, [ctypes.POINTER(Prep), _P, _I64, _I64, _P, _P, _I32, _I32, _I32,
                                   _P, _I32, _I32, _P, _I64, _I64, _I64, _P]),
     "wa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -188,6 +192,38 @@ def prompt(q, k, v, p0, win, ring, scale=1.0, hi=None, p32=False, out=None, work
                            k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
                            int(p0), n, hq, hkv, d, hp, wp, wn, out.data_ptr(), out.stride(0),
                            out.stride(1), _stream()))
+    return out
+
+
+def prompt_sparse(q, k, v, p0, win, ring, masks, scale=1.0, hi=None, p32=False, out=None,
+                  workspace=None):
+    """Block-sparse prompt rows p0 .. p0+n-1 (wa_prompt_sparse): as ``prompt``, and row i sees
+    only the keys whose 64-key block is selected in masks[i] (int32/uint32 words as an int32
+    CUDA tensor [n, words], unit word stride)."""
+    _bf16(q, "q"); _bf16(k, "k"); _bf16(v, "v")
+    if k.shape != v.shape or k.stride() != v.stride() or k.dim() != 3:
+        raise ValueError("k and v must share one [ring, Hkv, d] layout")
+    if masks.dtype != torch.int32 or not masks.is_cuda or masks.dim() != 2 or masks.stride(1) != 1:
+        raise TypeError("masks must be an int32 CUDA tensor [n, words] with unit word stride")
+    n, hq, d = q.shape
+    ring_k, hkv, dk = k.shape
+    if dk != d or ring_k < ring or masks.shape[0] != n:
+        raise ValueError("k/v/masks shape does not match q or the ring length")
+    hp = None
+    if hi is not None:
+        _i32(hi, "hi")
+        hp = hi.data_ptr()
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.bfloat16, device=q.device)
+    w = window(win, ring, scale, p32)
+    need = lib().wa_prompt_sparse_workspace(ctypes.byref(w), int(p0), n, hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().wa_prompt_sparse(ctypes.byref(w), q.data_ptr(), q.stride(0), q.stride(1),
+                                  k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
+                                  int(p0), n, hq, hkv, d, hp, masks.data_ptr(), masks.stride(0),
+                                  masks.shape[1], workspace.data_ptr(), workspace.numel(),
+                                  out.data_ptr(), out.stride(0), out.stride(1), _stream()))
     return out
 
 

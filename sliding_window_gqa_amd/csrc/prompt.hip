@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     __shared__ __attribute__((aligned(1024))) char Ks1[TILE_B];
     __shared__ __attribute__((aligned(1024))) char Vs1[TILE_B];
     __shared__ int red_i[2][kWaves];
+    __shared__ uint32_t red_sel[kWaves];
 
     // XCD-aware remap of the linear workgroup index
     const int total = gridDim.x;
@@ -179,13 +180,49 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     if (kmax < kmin) return;                // no valid pair in this workgroup
     // split mode: this workgroup takes the key chunk cidx of its range, at absolute
     // positions, and writes per-chunk partials that a merge combines in chunk order
-    const bool split = a.nchunk > 1;
+    const bool split = a.nchunk > 1 || a.bm != nullptr;
     const int chunk = kmin / kPromptChunk + cidx;
     if (split) {
         kmin = max(kmin, chunk * kPromptChunk);
         kmax = min(kmax, chunk * kPromptChunk + kPromptChunk - 1);
         if (kmax < kmin) return;
     }
+    const int t0 = kmin / BN, t1 = kmax / BN;
+
+    // Block-sparse prompts (always split, so t1 - t0 < 6): bit i of `eff` says that tile
+    // t0 + i is selected by this lane's row and meets its key range; the workgroup walks
+    // only the union of its rows' tiles, a wave computes only its own union, and a lane
+    // masks the tiles its row did not select.
+    const bool sparse = a.bm != nullptr;
+    uint32_t eff = 0, w_any = 0, w_every = 0, tiles = 0;
+    if (sparse) {
+        if (valid) {
+            const uint32_t* brow = a.bm + (int64_t)row * a.bm_srow;
+            for (int b = t0; b <= t1; ++b)
+                if (block_selected(brow, a.bm_words, b) && BN * b <= last && BN * b + BN - 1 >= lo)
+                    eff |= 1u << (b - t0);
+        }
+        w_any = eff;                        // tiles some lane of the wave needs
+        w_every = valid ? eff : ~0u;        // tiles every valid lane of the wave selected
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            w_any |= (uint32_t)__shfl_xor((int)w_any, m, 64);
+            w_every &= (uint32_t)__shfl_xor((int)w_every, m, 64);
+        }
+        if (lane == 0) red_sel[wave] = w_any;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tiles |= red_sel[w];
+        if (tiles == 0) return;             // none of the workgroup's rows selected a tile here
+    }
+    // the i-th tile the workgroup walks, and how many
+    auto tile_at = [&](int i) {
+        if (!sparse) return t0 + i;
+        uint32_t x = tiles;
+        for (int k = 0; k < i; ++k) x &= x - 1;
+        return x ? t0 + __builtin_ctz(x) : t1;     // past the last tile: a placeholder, unused
+    };
+    const int ntiles = sparse ? __builtin_popcount(tiles) : t1 - t0 + 1;
 
     // Q^T operand (loaded at the start): a negative scale is carried by q's sign (exact), so
     // the exponent factor is positive and the row maximum of the raw scores gives the
@@ -280,11 +317,14 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 
     // one tile: start the next tile's loads into the other stage, compute on this stage,
     // then wait for the loads and meet at the barrier
-    auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more) {
+    auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more,
+                    int next) {
         const int base = tile * BN;
-        if (more) issue_tile(tile + 1, knext, vnext);
-        // this wave computes only if the tile meets its key range
-        if (base <= w_kmax && base + BN - 1 >= w_kmin) {
+        if (more) issue_tile(next, knext, vnext);
+        // this wave computes only if the tile meets its key range (and, sparse, its rows'
+        // selection)
+        const uint32_t tbit = sparse ? 1u << (tile - t0) : 0u;
+        if (base <= w_kmax && base + BN - 1 >= w_kmin && (!sparse || (w_any & tbit))) {
             // S^T = K Q^T for two 32-key halves
             // the two 32-key halves alternate, so each LDS read has two MFMAs to hide behind
             f32x16 sacc[2];
@@ -320,14 +360,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
             // online softmax; t = s * scale * log2(e) is formed inside the exponent's fma
-            const bool full = base >= w_loall && base + BN - 1 <= w_lastall;
+            const bool full = base >= w_loall && base + BN - 1 <= w_lastall && (!sparse || (w_every & tbit));
+            const bool lsel = !sparse || (eff & tbit);
             if (!full) {
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kpos = base + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
-                        if (kpos < lo || kpos > last) sacc[mb][r] = -INFINITY;
+                        if (kpos < lo || kpos > last || !lsel) sacc[mb][r] = -INFINITY;
                     }
             }
             float smax = -INFINITY;
@@ -403,19 +444,21 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         __syncthreads();
     };
 
-    const int t0 = kmin / BN, t1 = kmax / BN;
-    issue_tile(t0, Ks0, Vs0);
+    issue_tile(tile_at(0), Ks0, Vs0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int tile = t0; tile <= t1; tile += 2) {
-        step(tile, Ks0, Vs0, Ks1, Vs1, tile < t1);
-        if (tile + 1 <= t1) step(tile + 1, Ks1, Vs1, Ks0, Vs0, tile + 1 < t1);
+    for (int i = 0; i < ntiles; i += 2) {
+        step(tile_at(i), Ks0, Vs0, Ks1, Vs1, i + 1 < ntiles, tile_at(i + 1));
+        if (i + 1 < ntiles) step(tile_at(i + 1), Ks1, Vs1, Ks0, Vs0, i + 2 < ntiles, tile_at(i + 2));
     }
 
     // epilogue: O / l, one rounding to bf16; in split mode the chunk's (m, l, O) partial
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (split) {
-        if (valid && lo <= chunk * kPromptChunk + kPromptChunk - 1 && last >= chunk * kPromptChunk) {
+        // the partial of a chunk holding at least one of the row's keys (sparse: of its
+        // selected blocks); the merge reads exactly these
+        if (valid && lo <= chunk * kPromptChunk + kPromptChunk - 1 && last >= chunk * kPromptChunk &&
+            (!sparse || eff != 0)) {
             const int64_t pi = ((int64_t)row * a.hq + head) * a.Cp + (chunk - lo / kPromptChunk);
             if (h == 0) { a.pm[pi] = m_run; a.pl[pi] = l_tot; }
             float* op = a.po + pi * D;
@@ -477,10 +520,23 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         int nc = last / kPromptChunk - lo / kPromptChunk + 1;
         nc = nc > a.Cp ? a.Cp : nc;
         const int64_t pi = pr * a.Cp;     // (row * hq + head) * Cp
+        // Does chunk c (of the row's range) hold one of the row's keys? Every chunk of a
+        // dense range does; a sparse row's chunk only through a selected block that meets
+        // [lo, last] -- the rule the prompt kernel writes partials by.
+        const uint32_t* brow = a.bm ? a.bm + (int64_t)row * a.bm_srow : nullptr;
+        auto present = [&](int c) {
+            if (c >= nc) return false;
+            if (!brow) return true;
+            const int c0 = (lo / kPromptChunk + c) * (kPromptChunk / kSparseBlock);
+            for (int b = c0; b < c0 + kPromptChunk / kSparseBlock; ++b)
+                if (block_selected(brow, a.bm_words, b) && kSparseBlock * b <= last && kSparseBlock * b + kSparseBlock - 1 >= lo)
+                    return true;
+            return false;
+        };
         // chunks in blocks of 64, lane c of a block holding chunk (m, l)
         float M = -INFINITY;
         for (int cb = 0; cb < nc; cb += 64)
-            M = fmaxf(M, cb + lane < nc ? a.pm[pi + cb + lane] : -INFINITY);
+            M = fmaxf(M, present(cb + lane) ? a.pm[pi + cb + lane] : -INFINITY);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
         float num[DL], den = 0.f;
@@ -488,16 +544,17 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         for (int e = 0; e < DL; ++e) num[e] = 0.f;
         const float* op = a.po + pi * D + DL * lane;
         for (int cb = 0; cb < nc; cb += 64) {
-            const bool in = cb + lane < nc;
+            const bool in = present(cb + lane);
             const float ac = __builtin_amdgcn_exp2f((in ? a.pm[pi + cb + lane] : -INFINITY) - M);
             const float lc = in ? a.pl[pi + cb + lane] : 0.f;
+            const uint64_t inmask = __ballot(in);
             const int ce = min(nc - cb, 64);
             // eight chunks' o loads in flight at a time, then their fmas in chunk order
             for (int cg = 0; cg < ce; cg += 8) {
                 float o[8][DL];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if (cg + j < ce) {
+                    if (cg + j < ce && ((inmask >> (cg + j)) & 1)) {
                         const float* oc = op + (int64_t)(cb + cg + j) * D;
                         if constexpr (DL == 4) {
                             const float4 v = *reinterpret_cast<const float4*>(oc);
@@ -510,7 +567,7 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if (cg + j < ce) {
+                    if (cg + j < ce && ((inmask >> (cg + j)) & 1)) {
                         const float ac_c = __shfl(ac, cg + j, 64);
                         const float l_c = __shfl(lc, cg + j, 64);
 #pragma unroll
@@ -550,7 +607,8 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
         const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
         rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
-                     a.kv_sslot, a.ring, lo, last, a.scale, orow);
+                     a.kv_sslot, a.ring, lo, last, a.scale, orow,
+                     a.bm ? a.bm + (int64_t)row * a.bm_srow : nullptr, a.bm_words);
         __syncthreads();
     }
 }
@@ -621,7 +679,7 @@ hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t npairs = (int64_t)a.n * a.hq;
-    if (a.nchunk > 1)
+    if (a.nchunk > 1 || a.bm)
         hipLaunchKernelGGL((prompt_merge_kernel<D>), dim3((unsigned)((npairs + kMergePairs - 1) / kMergePairs)),
                            dim3(D), 0, s, a);
     else {

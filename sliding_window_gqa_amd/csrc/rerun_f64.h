@@ -10,7 +10,8 @@
 //
 // One workgroup of D threads per (row, head), D = head dim: scores in float64 as plain
 // dim-order sums of exact bf16 -> f64 products, max, exp, l = sum p, x_d = sum p v_d / l,
-// keys outside [lo, last] never touched, sums started at +0, one rounding to bf16.
+// keys outside [lo, last] (or in unselected blocks) never touched, sums started at +0, one
+// rounding to bf16; a (row, head) with no key gives 0 / 0 = NaN.
 #pragma once
 
 #include "wa_common.h"
@@ -36,10 +37,13 @@ __device__ __forceinline__ bool any_nonfinite(const uint16_t* out) {
 }
 
 // The float64 re-run. q: the head's query row; kb, vb: key/value base of the key head
-// (slot 0); sslot: slot stride; keys lo..last, key j in slot j mod ring.
+// (slot 0); sslot: slot stride; keys lo..last, key j in slot j mod ring; with a block mask
+// (bm, words; nullptr: none) only the keys of selected 64-key blocks.
 template <int D>
 __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t* vb,
-                          int64_t sslot, int ring, int lo, int last, float scale, uint16_t* out) {
+                          int64_t sslot, int ring, int lo, int last, float scale, uint16_t* out,
+                          const uint32_t* bm = nullptr, int words = 0) {
+    auto sel = [&](int j) { return bm == nullptr || block_selected(bm, words, j / kSparseBlock); };
     __shared__ double qs[D];
     __shared__ double ps[D];
     __shared__ double red[D];
@@ -55,7 +59,8 @@ __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t*
     };
     // pass 1: the maximum score (a NaN score reaches the output through its weight)
     double mx = -INFINITY;
-    for (int j = lo + t; j <= last; j += D) mx = fmax(mx, score(j));
+    for (int j = lo + t; j <= last; j += D)
+        if (sel(j)) mx = fmax(mx, score(j));
     red[t] = mx;
     __syncthreads();
     for (int w = D / 2; w > 0; w >>= 1) {
@@ -69,14 +74,14 @@ __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t*
     for (int base = lo; base <= last; base += D) {
         const int j = base + t;
         double p = 0.0;
-        if (j <= last) p = exp(score(j) - m);
+        if (j <= last && sel(j)) p = exp(score(j) - m);
         ps[t] = p;
         l += p;
         __syncthreads();
         const int nk = min(D, last - base + 1);
         for (int i = 0; i < nk; ++i) {
             const int jj = base + i;
-            x += ps[i] * (double)bf16_to_f32(vb[(int64_t)(jj % ring) * sslot + t]);
+            if (sel(jj)) x += ps[i] * (double)bf16_to_f32(vb[(int64_t)(jj % ring) * sslot + t]);
         }
         __syncthreads();
     }

@@ -152,6 +152,57 @@ int wa_prompt(const wa_window_t* w,
     return WA_OK;
 }
 
+size_t wa_prompt_sparse_workspace(const wa_window_t* w, int32_t p0, int32_t n, int32_t hq, int32_t d) {
+    if (!window_ok(w) || p0 < 0 || n <= 0 || hq <= 0 || (d != 128 && d != 256)) return 0;
+    if ((int64_t)p0 + n > 0x7FFFFFFF) return 0;
+    const size_t cells = (size_t)n * (size_t)hq * (size_t)wa::sparse_chunks(w->window, p0, n);
+    return cells * sizeof(float) * (2 + (size_t)d) + 16;
+}
+
+int wa_prompt_sparse(const wa_window_t* w,
+                     const uint16_t* q, int64_t q_srow, int64_t q_shead,
+                     const uint16_t* k, const uint16_t* v, int64_t kv_sslot, int64_t kv_shead,
+                     int32_t p0, int32_t n, int32_t hq, int32_t hkv, int32_t d,
+                     const int32_t* hi, const uint32_t* blocks, int64_t blocks_srow, int32_t blocks_words,
+                     void* ws, size_t ws_bytes,
+                     uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    if (!blocks || blocks_words <= 0 || blocks_srow < blocks_words) return WA_EARG;
+    if ((uintptr_t)blocks & 3) return WA_EARG;
+    if (!w || !q || !k || !v || !out) return WA_EARG;
+    if (n <= 0 || p0 < 0) return WA_EARG;
+    if (q_srow < 0 || q_shead < 0 || kv_sslot < 0 || kv_shead < 0 || o_srow < 0 || o_shead < 0)
+        return WA_EARG;
+    if (!head_shape_ok(hq, hkv, d)) return WA_EUNSUPPORTED;
+    if (!window_ok(w)) return WA_EARG;
+    if (w->p32 != WA_P_BF16 && w->p32 != WA_P_TWO && w->p32 != WA_P_THREE) return WA_EUNSUPPORTED;
+    if ((int64_t)p0 + n > 0x7FFFFFFF || (int64_t)n + w->window > 0x3FFFFFFF) return WA_ERANGE;
+    const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
+    if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
+    if ((q_srow | q_shead | kv_sslot | kv_shead) & 7) return WA_EARG;
+    if (((uintptr_t)out & 7) || ((o_srow | o_shead) & 3)) return WA_EARG;
+    const size_t need = wa_prompt_sparse_workspace(w, p0, n, hq, d);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return WA_EWORKSPACE;
+
+    wa::PromptArgs a{};
+    a.q = q; a.q_srow = q_srow; a.q_shead = q_shead;
+    a.k = k; a.v = v; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
+    a.p0 = p0; a.n = n; a.hq = hq; a.hkv = hkv; a.d = d;
+    a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p_parts = 1 + w->p32;
+    a.hi = hi;
+    a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
+    a.bm = blocks; a.bm_srow = blocks_srow; a.bm_words = blocks_words;
+    a.nchunk = wa::sparse_chunks(w->window, p0, n);
+    a.Cp = a.nchunk;
+    const size_t cells = (size_t)n * hq * a.Cp;
+    a.pm = static_cast<float*>(ws);
+    a.pl = a.pm + cells;
+    a.po = a.pl + cells;
+    if (((uintptr_t)a.po) & 15) a.po = reinterpret_cast<float*>(((uintptr_t)a.po + 15) & ~(uintptr_t)15);
+    if (wa::launch_prompt(a, static_cast<hipStream_t>(stream)) != hipSuccess) return WA_EHIP;
+    return WA_OK;
+}
+
 int wa_prepare(const wa_prep_t* p,
                const uint16_t* x, int64_t x_srow, int64_t x_shead,
                const int32_t* pos_of_row, const float* qs,

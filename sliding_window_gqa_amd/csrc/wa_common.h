@@ -59,7 +59,19 @@ struct PromptArgs {
     // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials
     int32_t nchunk, Cp;
     float* pm; float* pl; float* po;
+    // block-sparse prompts: row i sees only the keys of its range whose 64-key block b has
+    // bit b % 32 of word b / 32 set in bm[i * bm_srow ..] (words past bm_words: not
+    // selected); bm == nullptr: every key of the range
+    const uint32_t* bm; int64_t bm_srow; int32_t bm_words;
 };
+
+constexpr int kSparseBlock = 64;   // keys per selectable block (= the prompt kernel's key tile)
+
+// is block b selected in a row's mask?
+__device__ __forceinline__ bool block_selected(const uint32_t* row_mask, int words, int b) {
+    const int w = b >> 5;
+    return w < words && ((row_mask[w] >> (b & 31)) & 1u) != 0;
+}
 
 // prompt split: keys [384c, 384c + 383], absolute (six 64-key tiles: a 1024-key window over a
 // 512-row chunk then fills the GPU in one round of workgroups)
@@ -81,6 +93,11 @@ struct PrepArgs {
 // (a row's last key is at most p0 + n - 1, so its range spans at most window - 1 + n keys).
 inline int prompt_wg_chunks(int window, int n) { return (window - 1 + n) / kPromptChunk + 2; }
 inline int prompt_pair_chunks(int window, int n) { return (window - 1 + n) / kPromptChunk + 2; }
+// Sparse prompts are always split; without a window a row's range starts at key 0, so its
+// chunks, and a workgroup's, are those of keys 0 .. p0 + n - 1.
+inline int sparse_chunks(int window, int p0, int n) {
+    return window > 0 ? prompt_pair_chunks(window, n) : (p0 + n - 1) / kPromptChunk + 1;
+}
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_decode_part(const DecodeArgs& a, hipStream_t s);

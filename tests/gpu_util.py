@@ -87,3 +87,25 @@ def compare(out, x, S, e_p, label):
             t = tuple(idx)
             log(f"  fail at {t}: out=0x{int(out[t]):04x} x={x[t]!r} S={S[t]!r}")
     return rep, ok
+
+
+def run_sparse(case, p32=None, rows=None, masks=None):
+    """Run a block-sparse prompt case (``case.masks``, or ``masks``); ``rows`` = (a, b)
+    runs only rows a..b-1 as their own call."""
+    from sliding_window_gqa_amd import api
+    p32 = case.p32 if p32 is None else p32
+    masks = case.masks if masks is None else masks
+    a, b = (0, case.n) if rows is None else rows
+    q = dev_bf16(case.q)[a:b]
+    k = dev_bf16(case.k)
+    v = dev_bf16(case.v)
+    hi = None if case.hi is None else dev_i32(case.hi[a:b])
+    m = torch.from_numpy(np.ascontiguousarray(masks[a:b]).view(np.int32)).cuda()
+    out = api.prompt_sparse(q, k, v, case.p0 + a, case.win, case.ring, m, case.scale, hi=hi, p32=p32)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+def oracle_sparse(case, rows=None, masks=None):
+    return attend.sparse_prompt(case.q, case.k, case.v, case.p0, case.win, case.ring, case.scale,
+                                case.masks if masks is None else masks, hi=case.hi, rows=rows)

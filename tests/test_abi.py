@@ -115,6 +115,31 @@ def test_prompt_rejects_before_launch():
     assert _prompt(api.window(1024, 1536, p32=-1)) == WA_EUNSUPPORTED
 
 
+def _sparse(w, blocks=FAKE, srow=4, words=4, ws_bytes=1 << 30, p0=0, n=10):
+    L = api.lib()
+    return L.wa_prompt_sparse(ctypes.byref(w), FAKE, 1024, 256, FAKE, FAKE, 512, 256, p0, n, 4, 2,
+                              256, None, blocks, srow, words, FAKE, ws_bytes, FAKE, 1024, 256, None)
+
+
+def test_prompt_sparse_rejects_before_launch():
+    w = api.window(0, 4096)
+    assert _sparse(w, blocks=None) == WA_EARG
+    assert _sparse(w, words=0) == WA_EARG
+    assert _sparse(w, srow=3) == WA_EARG                       # a row's words overlap the next
+    assert _sparse(w, blocks=FAKE + 2) == WA_EARG
+    assert _sparse(api.window(0, 4096, p32=3)) == WA_EUNSUPPORTED
+    assert _sparse(w, p0=4090) == WA_ERANGE                    # keys up to 4099 in a 4096 ring
+    need = api.lib().wa_prompt_sparse_workspace(ctypes.byref(w), 0, 10, 4, 256)
+    # without a window, chunks of keys 0 .. p0 + n - 1: (10 - 1) / 384 + 1 = 1 per (row, head)
+    assert need == 10 * 4 * 1 * 4 * (2 + 256) + 16
+    assert _sparse(w, ws_bytes=need - 1) == WA_EWORKSPACE
+    w1 = api.window(1024, 1536)
+    assert api.lib().wa_prompt_sparse_workspace(ctypes.byref(w1), 5000, 512, 16, 256) == \
+        api.lib().wa_prompt_workspace(ctypes.byref(w1), 512, 16, 256)
+    big = api.lib().wa_prompt_sparse_workspace(ctypes.byref(api.window(0, 8000)), 7836, 64, 24, 256)
+    assert big == 64 * 24 * (7899 // 384 + 1) * 4 * (2 + 256) + 16
+
+
 def test_prompt_workspace_sizes():
     L = api.lib()
     w = api.window(1024, 1536)
