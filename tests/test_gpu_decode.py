@@ -89,6 +89,30 @@ def test_decode_invariants():
         assert np.array_equal(gu.run_decode(case), full)
 
 
+@pytest.mark.parametrize("rows,hq,hkv,win,ring,streams", [
+    (40, 16, 8, 1536, 1536, 2),    # window = ring: a row's chunks c and c + 6 share a slot block
+    (33, 4, 4, 0, 1024, 3),        # linear cache, one query head per key head
+    (20, 8, 4, 700, 768, 1),       # every row in one stream: groups of 8 rows
+    (64, 16, 8, 1024, 1536, 3),    # the 12B shape
+])
+def test_rows_sharing_streams_match_rows_alone(rows, hq, hkv, win, ring, streams):
+    """Many rows on few streams (a row meeting one slot block twice at window = ring, window 0,
+    one query head per key head): each row's bits equal those it gets alone in its own call,
+    whichever decode kernel each call takes, and pass the gate."""
+    rng = np.random.default_rng(rows + win)
+    hi = ring - 1 if win == 0 else 20000
+    pos = rng.integers(0, hi + 1, size=rows)
+    pos[:4] = [0, 255, 256, min(hi, 1535)]
+    case = workloads.decode_case("shared", rows, hq, hkv, 256, win, ring, streams, pos,
+                                 seed=rows * 3 + hq, peak_every=3)
+    full, _ = _gate(case, f"shared streams {rows}x{hq}/{hkv} win{win} ring{ring} streams{streams}")
+    for r in range(rows):
+        t = int(case.stream[r])
+        one = workloads.DecodeCase("alone", case.q[r:r + 1], case.k[t:t + 1], case.v[t:t + 1],
+                                   np.array([0], np.int32), case.pos[r:r + 1], case.win, case.ring)
+        assert np.array_equal(gu.run_decode(one)[0], full[r]), r
+
+
 @pytest.mark.parametrize("rows,hq,hkv,d,win,ring,streams", [SHAPES[1], SHAPES[3], (64, 16, 8, 256, 1024, 1536, 3)])
 def test_merge_reproduces_decode(rows, hq, hkv, d, win, ring, streams):
     """wa_merge on the partials wa_decode leaves in its workspace (layout of the header:
