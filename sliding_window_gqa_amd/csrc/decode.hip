@@ -18,11 +18,13 @@
 //   softmax one wave per query head: 4 keys per lane, wave butterflies for max and sum.
 //   P.V     fp32 on the VALU: each run is an fma chain in key order over its keys, 8 dims a
 //           lane; the runs are summed in run order through LDS.
-//   loads   K and V arrive in 16-key units (16 x 16 bytes per lane) through two register
-//           buffers, each refilled with the unit two places ahead as soon as it is consumed.
+//   loads   K and V arrive in 16-key units (16 x 16 bytes per lane) through one register
+//           buffer, refilled with the next unit as soon as it is consumed (16 loads a lane
+//           in flight; 32, through two buffers, streamed slower).
 //   kernels decode_kernel<.., false>: one workgroup per (row, key head, chunk), partials to
-//           memory, then merge_kernel; decode_kernel<.., true>: for large batches, one
-//           workgroup per (row, key head) walks the row's chunks and merges them itself.
+//           memory, then merge_kernel; decode_kernel<.., true>: for large batches of rows
+//           that do not share rings, one workgroup per (row, key head) walks the row's
+//           chunks and merges them itself.
 //           Both run the same per-chunk code and the same merge arithmetic, so a row's bits
 //           do not depend on which one ran it (nor on the batch, the slot or the ring size).
 //   grid    workgroup ids remapped so that each XCD works on the rows of a few key heads and
@@ -134,14 +136,13 @@ __device__ __forceinline__ float unit_sum(const float (&v)[16], int dl) {
 }
 
 template <int D, int GMAX, bool WHOLE>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_kernel(DecodeArgs a) {
     constexpr int LPK = D / 8;               // lanes per key: 8 dims a lane
     constexpr int NRUN = kThreads / LPK;     // runs of consecutive keys per chunk
     constexpr int RUNLEN = kChunk / NRUN;    // keys per run
     constexpr int NU = RUNLEN / 16;          // 16-key load units per run, for K and for V
     constexpr int GH = GMAX < 4 ? GMAX : 4;  // heads per LDS reduction pass
     constexpr int CM = WHOLE ? kRowCMax : 1;
-    constexpr bool TWO = GMAX <= 4;          // two load buffers (else one: register budget)
     static_assert(!WHOLE || (D == 256 && GMAX <= 2), "whole rows: d = 256, at most two query heads per key head");
     static_assert(NU == 1 || NU == 2, "runs of 16 or 32 keys");
 
@@ -319,31 +320,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         }
     };
 
-    uint4 X[16], Y[TWO ? 16 : 1];
+    // one register buffer: 16 loads a lane in flight (two buffers, 32 in flight, measured
+    // slower on this part's memory system)
+    uint4 X[16];
     Chunk cur = chunk_at(k0);
     issue(cur, 0, true, X);
-    if constexpr (TWO) issue(cur, 1, true, Y);
     for (int k = k0; k < k0 + nch; ++k) {
         const int ks = k - k0;                   // chunk slot within this workgroup
         const bool more = k + 1 < k0 + nch;
         const Chunk nxt = chunk_at(more ? k + 1 : k);
-        // ---- scores; the freed buffers take the chunk's V (or, at d = 128, the next K)
-        if constexpr (!TWO) {
-            consume_k(cur, 0, X);
-            if constexpr (NU == 2) {
-                issue(cur, 1, true, X);
-                consume_k(cur, 1, X);
-            }
-            issue(cur, NU, true, X);
-        } else if constexpr (NU == 2) {
-            consume_k(cur, 0, X);
-            issue(cur, 2, true, X);
-            consume_k(cur, 1, Y);
-            issue(cur, 3, true, Y);
-        } else {
-            consume_k(cur, 0, X);
-            if (WHOLE) issue(nxt, 0, more, X);
+        // ---- scores; each consumed unit frees the buffer for the next: K units, then V
+        consume_k(cur, 0, X);
+        if constexpr (NU == 2) {
+            issue(cur, 1, true, X);
+            consume_k(cur, 1, X);
         }
+        issue(cur, NU, true, X);
         __syncthreads();
         // ---- chunk softmax: m_c, p = expf(s - m_c), l_c, one wave per head
         for (int h = wave; h < G; h += 4) {
@@ -383,21 +375,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
         for (int h = 0; h < GMAX; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        if constexpr (!TWO) {
-            consume_v(cur, 0, X);
-            if constexpr (NU == 2) {
-                issue(cur, NU + 1, true, X);
-                consume_v(cur, 1, X);
-            }
-        } else if constexpr (NU == 2) {
-            consume_v(cur, 0, X);
-            if (WHOLE) issue(nxt, 0, more, X);
-            consume_v(cur, 1, Y);
-            if (WHOLE) issue(nxt, 1, more, Y);
-        } else {
-            consume_v(cur, 0, Y);
-            if (WHOLE) issue(nxt, 1, more, Y);
+        consume_v(cur, 0, X);
+        if constexpr (NU == 2) {
+            issue(cur, NU + 1, true, X);
+            consume_v(cur, 1, X);
         }
+        if (WHOLE) issue(nxt, 0, more, X);   // the next chunk's first K unit
         // ---- runs summed in run order, GH heads per pass
 #pragma unroll
         for (int hp = 0; hp < GMAX; hp += GH) {
@@ -577,10 +560,12 @@ hipError_t launch_part_d(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Whole rows for large batches of rows that do not share rings; rows sharing rings read
+// their keys from L2 and run faster as chunk workgroups (more of them in flight per CU).
 bool decode_whole_rows(const DecodeArgs& a) {
     const int G = a.hq / a.hkv;
     return a.d == 256 && G <= 2 && a.C <= kRowCMax && (int64_t)a.rows * a.hkv >= kRowMinWG &&
-           a.ring >= kChunk && (a.ring & 15) == 0;
+           a.streams >= a.rows && a.ring >= kChunk && (a.ring & 15) == 0;
 }
 
 }  // namespace

@@ -51,6 +51,7 @@ SHAPES = [
     (4, 8, 8, 128, 64, 100, 4),
     (3, 4, 2, 256, 0, 1300, 1),
     (8, 32, 16, 256, 1024, 1536, 2),
+    (3, 16, 1, 256, 300, 700, 2),         # sixteen query heads on one key head
 ]
 
 
