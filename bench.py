@@ -34,6 +34,7 @@ from sliding_window_gqa_amd import api, workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+VALU_FP32_PEAK_TFS = 157.3   # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 flop/clk, packed)
 CHUNK = 256
 
 
@@ -441,20 +442,28 @@ def main():
         "wall_s_timed_loop": round(wall, 3),
     }
     rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s",
-                         traffic_bytes("prompt12b", ["prompt_kernel"]))
-    rl_decode = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                         traffic_bytes("decode12b", ["decode_kernel", "merge_kernel"]))
-    rl_prompt["kernel"] = "prompt_kernel<256,p32> (12B prompt chunk)"
-    rl_decode["kernel"] = "decode_kernel<256,2,whole rows> (unique K/V bytes)"
+                         traffic_bytes("prompt12b", ["prompt_kernel", "prompt_merge_kernel"]))
+    rl_prompt["kernel"] = "prompt_kernel<256,p32> + prompt_merge_kernel (12B prompt chunk)"
+    # The rows share three rings: the per-row K/V reads come from L2/MALL and the call is
+    # bound by its fp32 VALU work (q.k and p.v fmas), not by HBM bytes; both views are given.
+    dec_tfs = du["flops_fp32"] / (dms * 1e-3) / 1e12
+    dec_traffic = traffic_bytes("decode12b", ["decode_kernel", "merge_kernel"])
+    rl_decode = roofline("alu", dec_tfs, VALU_FP32_PEAK_TFS, "TFLOP/s", dec_traffic)
+    rl_decode["kernel"] = "decode_kernel<256,2,chunks> + merge_kernel (fp32 q.k and p.v work)"
+    rl_decode_hbm = roofline("hbm", du["unique_bytes"] / (dms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                             dec_traffic)
+    rl_decode_hbm["kernel"] = "decode_kernel<256,2,chunks> + merge_kernel (unique K/V bytes)"
     res["roofline"] = rl_prompt if pms >= dms else rl_decode
     res["roofline_decode"] = rl_decode
+    res["roofline_decode_unique_bytes"] = rl_decode_hbm
+    res["roofline_prefill"] = rl_prompt
     hgbs = hu["row_bytes"] / (hms * 1e-3) / 1e9
     res["decode_64_streams"] = {"workload": "12B decode shape, 64 rows in 64 streams (no shared keys)",
                                 "ms": round(hms, 5), "bytes_per_call": hu["row_bytes"],
                                 "gbs": round(hgbs, 2)}
     rl_h = roofline("hbm", hgbs, HBM_PEAK_GBS, "GB/s",
                     traffic_bytes("decode12b64", ["decode_kernel", "merge_kernel"]))
-    rl_h["kernel"] = "decode_kernel<256,2,whole rows> (64 streams)"
+    rl_h["kernel"] = "decode_kernel<256,2,whole rows> (64 streams, no shared keys)"
     res["roofline_decode_64_streams"] = rl_h
 
     if not args.no_long:

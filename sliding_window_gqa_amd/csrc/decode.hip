@@ -479,35 +479,45 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
         int n = rs.c_hi - rs.c_lo + 1;
         n = n > a.C ? a.C : n;
         const int64_t pi = pr * a.C;      // (r * hq + h) * C
-        float M = -INFINITY;
-        for (int cb = 0; cb < n; cb += 64)
+        const float* op = a.o + pi * D + DL * lane;
+        // eight chunks' o at a time, chunk c0 + j from chunk c0 (j < cnt)
+        auto load8 = [&](float (&o)[8][DL], int c0, int cnt) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < cnt) {
+                    const float* oc = op + (int64_t)(c0 + j) * D;
+                    if constexpr (DL == 4) {
+                        const float4 v = *reinterpret_cast<const float4*>(oc);
+                        o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
+                    } else {
+                        const float2 v = *reinterpret_cast<const float2*>(oc);
+                        o[j][0] = v.x; o[j][1] = v.y;
+                    }
+                }
+            }
+        };
+        // the first 64 chunks' (m, l) and the first eight chunks' o are all requested
+        // before any is used: one memory round trip for the common row, not three
+        float o[8][DL];
+        load8(o, 0, min(n, 8));
+        const bool in0 = lane < n;
+        const float m0 = in0 ? a.m[pi + lane] : -INFINITY;
+        const float l0 = in0 ? a.l[pi + lane] : 0.f;
+        float M = fmaxf(-INFINITY, m0);
+        for (int cb = 64; cb < n; cb += 64)
             M = fmaxf(M, cb + lane < n ? a.m[pi + cb + lane] : -INFINITY);
         M = wave_max(M);
         float num[DL], den = 0.f;
 #pragma unroll
         for (int e = 0; e < DL; ++e) num[e] = 0.f;
-        const float* op = a.o + pi * D + DL * lane;
         for (int cb = 0; cb < n; cb += 64) {
             const bool in = cb + lane < n;
-            const float ac = expf((in ? a.m[pi + cb + lane] : -INFINITY) - M);
-            const float lc = in ? a.l[pi + cb + lane] : 0.f;
+            const float ac = expf((cb == 0 ? m0 : (in ? a.m[pi + cb + lane] : -INFINITY)) - M);
+            const float lc = cb == 0 ? l0 : (in ? a.l[pi + cb + lane] : 0.f);
             const int ce = min(n - cb, 64);
             // eight chunks' o loads in flight at a time, then their fmas in chunk order
             for (int cg = 0; cg < ce; cg += 8) {
-                float o[8][DL];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (cg + j < ce) {
-                        const float* oc = op + (int64_t)(cb + cg + j) * D;
-                        if constexpr (DL == 4) {
-                            const float4 v = *reinterpret_cast<const float4*>(oc);
-                            o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
-                        } else {
-                            const float2 v = *reinterpret_cast<const float2*>(oc);
-                            o[j][0] = v.x; o[j][1] = v.y;
-                        }
-                    }
-                }
+                if (cb + cg > 0) load8(o, cb + cg, ce - cg);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (cg + j < ce) {

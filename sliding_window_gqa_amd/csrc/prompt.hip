@@ -533,38 +533,48 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
                     return true;
             return false;
         };
-        // chunks in blocks of 64, lane c of a block holding chunk (m, l)
-        float M = -INFINITY;
-        for (int cb = 0; cb < nc; cb += 64)
+        const float* op = a.po + pi * D + DL * lane;
+        // eight chunks' o at a time, chunk c0 + j from chunk c0 (j < cnt, present ones)
+        auto load8 = [&](float (&o)[8][DL], int c0, int cnt, uint64_t inmask) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < cnt && ((inmask >> j) & 1)) {
+                    const float* oc = op + (int64_t)(c0 + j) * D;
+                    if constexpr (DL == 4) {
+                        const float4 v = *reinterpret_cast<const float4*>(oc);
+                        o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
+                    } else {
+                        const float2 v = *reinterpret_cast<const float2*>(oc);
+                        o[j][0] = v.x; o[j][1] = v.y;
+                    }
+                }
+            }
+        };
+        // chunks in blocks of 64, lane c of a block holding chunk (m, l); the first block's
+        // (m, l) and its first eight chunks' o are requested before any is used
+        const bool in0 = present(lane);
+        const uint64_t inmask0 = __ballot(in0);
+        float o[8][DL];
+        load8(o, 0, min(nc, 8), inmask0);
+        const float m0 = in0 ? a.pm[pi + lane] : -INFINITY;
+        const float l0 = in0 ? a.pl[pi + lane] : 0.f;
+        float M = fmaxf(-INFINITY, m0);
+        for (int cb = 64; cb < nc; cb += 64)
             M = fmaxf(M, present(cb + lane) ? a.pm[pi + cb + lane] : -INFINITY);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
         float num[DL], den = 0.f;
 #pragma unroll
         for (int e = 0; e < DL; ++e) num[e] = 0.f;
-        const float* op = a.po + pi * D + DL * lane;
         for (int cb = 0; cb < nc; cb += 64) {
-            const bool in = present(cb + lane);
-            const float ac = __builtin_amdgcn_exp2f((in ? a.pm[pi + cb + lane] : -INFINITY) - M);
-            const float lc = in ? a.pl[pi + cb + lane] : 0.f;
-            const uint64_t inmask = __ballot(in);
+            const bool in = cb == 0 ? in0 : present(cb + lane);
+            const float ac = __builtin_amdgcn_exp2f((cb == 0 ? m0 : (in ? a.pm[pi + cb + lane] : -INFINITY)) - M);
+            const float lc = cb == 0 ? l0 : (in ? a.pl[pi + cb + lane] : 0.f);
+            const uint64_t inmask = cb == 0 ? inmask0 : __ballot(in);
             const int ce = min(nc - cb, 64);
             // eight chunks' o loads in flight at a time, then their fmas in chunk order
             for (int cg = 0; cg < ce; cg += 8) {
-                float o[8][DL];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (cg + j < ce && ((inmask >> (cg + j)) & 1)) {
-                        const float* oc = op + (int64_t)(cb + cg + j) * D;
-                        if constexpr (DL == 4) {
-                            const float4 v = *reinterpret_cast<const float4*>(oc);
-                            o[j][0] = v.x; o[j][1] = v.y; o[j][2] = v.z; o[j][3] = v.w;
-                        } else {
-                            const float2 v = *reinterpret_cast<const float2*>(oc);
-                            o[j][0] = v.x; o[j][1] = v.y;
-                        }
-                    }
-                }
+                if (cb + cg > 0) load8(o, cb + cg, ce - cg, inmask >> cg);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (cg + j < ce && ((inmask >> (cg + j)) & 1)) {
