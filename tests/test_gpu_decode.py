@@ -300,3 +300,25 @@ def test_decode_nonfinite_whole_rows():
         one = workloads.DecodeCase("alone", case.q[rr:rr + 1], case.k[rr:rr + 1], case.v[rr:rr + 1],
                                    np.array([0], np.int32), case.pos[rr:rr + 1], case.win, case.ring)
         assert np.array_equal(gu.run_decode(one)[0], out[rr]), rr
+
+
+def test_fp32_accumulation_under_cancellation():
+    """Decode's fp32 P.V (fma chains in key order, runs summed in run order), measured: q = 0
+    gives every key the weight 1, and values in exactly cancelling +/- pairs of magnitudes
+    2^-20 .. 2^20 give an exact output of 0 over a 1,024-key window; the output is the
+    accumulation error, logged in units of 2^-24 S and held to the strict interval."""
+    from tests.test_gpu_prompt import _cancelling_values
+    rows, hq, hkv, d, win, ring = 6, 4, 2, 256, 1024, 1024
+    rng = np.random.default_rng(43)
+    pos = np.array([1023, 1023, 1023, 1023, 1023, 1023])
+    case = workloads.decode_case("cancellation", rows, hq, hkv, d, win, ring, rows, pos, seed=43,
+                                 peak_every=0)
+    case.q[:] = 0
+    for t in range(rows):
+        case.v[t] = _cancelling_values(rng, ring, hkv, d)
+    out = gu.run_decode(case)
+    x, S, _ = gu.oracle_decode(case)
+    got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = float(np.max(np.abs(got - x) / S))
+    gu.log(f"[decode fp32 accumulation] worst |out - x| / S = {worst:.3e} = {worst * 2 ** 24:.1f} x 2^-24")
+    assert check.accept(out, x, S, E_P, "S").all()

@@ -263,3 +263,39 @@ def test_prompt_inf_value_unseen_by_tile_neighbours(win, p32):
     x, S, _ = gu.oracle_prompt(case)
     assert np.isinf(x[:4, 0:2, 3]).all() and np.isfinite(x[4:]).all()
     assert check.accept(out, x, S, e_p(p32)).all()
+
+
+def _cancelling_values(rng, keys, heads, d):
+    """bf16 bits [keys, heads, d]: per (head, dim) column, keys/2 magnitudes 2^E (1 + F/128),
+    E uniform in -20..20, each placed once with + and once with - at random keys, so every
+    column sums to exactly 0 while its partial sums reach 2^20 and more."""
+    e = rng.integers(-20, 21, size=(keys // 2, heads, d))
+    f = rng.integers(0, 128, size=(keys // 2, heads, d))
+    mag = np.ldexp(1.0 + f / 128.0, e)
+    vals = np.concatenate([mag, -mag], axis=0)
+    for h in range(heads):
+        for c in range(d):
+            vals[:, h, c] = vals[rng.permutation(keys), h, c]
+    return workloads._bf16_bits(vals)
+
+
+@pytest.mark.parametrize("p32", [0, 1, 2])
+def test_mfma_accumulation_under_cancellation(p32):
+    """The matrix cores' fp32 accumulation, measured: q = 0 gives every key the weight 1
+    exactly (in every P representation), and values in exactly cancelling +/- pairs give an
+    exact output of 0, so a nonzero output is the accumulation error of P.V over 1,024 keys.
+    It is logged in units of 2^-24 S (S = mean |v|) and held to the strict interval of
+    e_P = 0, whose 2^-16 S allowance must cover it."""
+    n, hq, hkv, d, p0 = 24, 4, 4, 256, 1000
+    rng = np.random.default_rng(41 + p32)
+    case = workloads.prompt_case("cancellation", n, hq, hkv, d, p0, 0, p0 + n, seed=41,
+                                 hi=np.full(n, p0 + n - 1), p32=p32, peak_every=0)
+    case.q[:] = 0
+    case.v[:] = _cancelling_values(rng, p0 + n, hkv, d)
+    out = gu.run_prompt(case)
+    x, S, _ = gu.oracle_prompt(case)
+    got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = float(np.max(np.abs(got - x) / S))
+    gu.log(f"[mfma accumulation p32={p32}] worst |out - x| / S = {worst:.3e} "
+           f"= {worst * 2 ** 24:.1f} x 2^-24; allowance 2^-16 = 256 x 2^-24")
+    assert check.accept(out, x, S, check.E_P_THREE, "S").all()
