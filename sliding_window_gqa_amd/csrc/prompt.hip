@@ -26,7 +26,9 @@
 //     by buffer loads with a per-tile descriptor on interior tiles; K fragments are 16-byte
 //     LDS reads, V^T fragments come from the transposing LDS read (ds_read_b64_tr_b16); the
 //     tiles are double buffered, the next tile's loads are in flight while the current tile
-//     computes, and there is one barrier per tile;
+//     computes, and there is one barrier per tile; unsplit dense prompts at d = 128 walk the
+//     tiles software-pipelined (tile t + 1's score MFMAs are issued before tile t's softmax,
+//     K is fetched two tiles ahead and V one), with each tile's arithmetic unchanged;
 //   * the K rows of a tile are fed to the first MFMA in a permuted order so that the S^T
 //     accumulator registers of a lane are, eight at a time, exactly the B operand (P^T) the
 //     P.V MFMA needs for eight consecutive keys: no shuffles between the two products;
@@ -286,19 +288,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         lane_off[i] = (uint32_t)(r * a.kv_sslot + 8 * c) * 2u;
     }
     const int tile_extent = (int)((uint32_t)((BN - 1) * a.kv_sslot) * 2u + 2u * D);
-    auto issue_tile = [&](int tile, char* kdst, char* vdst) {
+    // loads of one tile of K (or V) into an LDS stage
+    auto issue_half = [&](int tile, char* dst, const uint16_t* src) __attribute__((always_inline)) {
         const int base = tile * BN;
         const int sbase = base % a.ring;
         if (base >= kmin && base + BN - 1 <= kmax && sbase + BN <= a.ring) {
             const int64_t toff = (int64_t)sbase * a.kv_sslot;
-            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + toff), (short)0, tile_extent, 0x00020000);
-            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + toff), (short)0, tile_extent, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + toff), (short)0, tile_extent, 0x00020000);
 #pragma unroll
-            for (int i = 0; i < NQ / kWaves; ++i) {
-                const int q = wave + kWaves * i;
-                buffer_to_lds16(kr, kdst + 1024 * q, lane_off[i]);
-                buffer_to_lds16(vr, vdst + 1024 * q, lane_off[i]);
-            }
+            for (int i = 0; i < NQ / kWaves; ++i) buffer_to_lds16(rs, dst + 1024 * (wave + kWaves * i), lane_off[i]);
             return;
         }
 #pragma unroll
@@ -310,146 +308,216 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             int slot = sbase + (jc - base);
             slot = slot >= a.ring ? slot - a.ring : slot;
             const int64_t off = (int64_t)slot * a.kv_sslot + 8 * c;
-            __builtin_amdgcn_global_load_lds(kg + off, (lds_void_ptr)(kdst + 1024 * q), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vg + off, (lds_void_ptr)(vdst + 1024 * q), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src + off, (lds_void_ptr)(dst + 1024 * q), 16, 0, 0);
         }
+    };
+    auto issue_tile = [&](int tile, char* kdst, char* vdst) __attribute__((always_inline)) {
+        issue_half(tile, kdst, kg);
+        issue_half(tile, vdst, vg);
+    };
+
+    // S^T of one tile into sacc (this wave's pairs; the tile must meet the wave's range)
+    auto scores = [&](const char* kt, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        // S^T = K Q^T for two 32-key halves
+        // the two 32-key halves alternate, so each LDS read has two MFMAs to hide behind
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
+        // K fragments are read two k-steps ahead of their MFMAs
+        Pack8 ka[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            ka[ks][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks]);
+            ka[ks][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const Pack8 a0 = ka[ks & 1][0], a1 = ka[ks & 1][1];
+            if (ks + 2 < KSTEPS) {
+                ka[ks & 1][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks + 2]);
+                ka[ks & 1][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks + 2]);
+            }
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0.v, qreg[ks].v, sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1.v, qreg[ks].v, sacc[1], 0, 0, 0);
+        }
+        // keep the reads two k-steps ahead in the instruction order: 4 reads, then
+        // (2 MFMAs, 2 reads) pairs, then the last 4 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks + 2 < KSTEPS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    };
+    // softmax of one tile's S^T (mask, lazy running maximum, exponentials, row sum, O rescale)
+    // and its P.V into O
+    // softmax head of one tile: mask (unless every pair sees the whole tile), the tile's
+    // maximum against the lazy running maximum, p = 2^(t - m) into sacc, and the row sum
+    struct Soft {
+        float m_new, mu, psum;
+        bool grow;
+    };
+    auto is_full = [&](int tile) __attribute__((always_inline)) {
+        const int base = tile * BN;
+        const uint32_t tbit = sparse ? 1u << (tile - t0) : 0u;
+        return base >= w_loall && base + BN - 1 <= w_lastall && (!sparse || (w_every & tbit));
+    };
+    auto soft_head = [&](int tile, f32x16 (&sacc)[2], bool full) __attribute__((always_inline)) {
+        const int base = tile * BN;
+        const uint32_t tbit = sparse ? 1u << (tile - t0) : 0u;
+        // online softmax; t = s * scale * log2(e) is formed inside the exponent's fma
+        const bool lsel = !sparse || (eff & tbit);
+        if (!full) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kpos = base + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
+                    if (kpos < lo || kpos > last || !lsel) sacc[mb][r] = -INFINITY;
+                }
+        }
+        float smax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[mb][r]);
+        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+        // lazy maximum: m moves only when the tile's maximum exceeds it by more than
+        // kLazy (log2 units), so p <= 2^kLazy and most tiles need no rescale of O
+        Soft sf;
+        const float m_cand = fmaxf(m_run, smax * cexp);
+        sf.grow = m_cand > m_run + kLazy;
+        sf.m_new = sf.grow ? m_cand : m_run;
+        sf.mu = (sf.m_new == -INFINITY) ? 0.f : sf.m_new;
+        sf.psum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], cexp, -sf.mu));
+                sacc[mb][r] = p;
+                sf.psum += p;
+            }
+        return sf;
+    };
+    // softmax tail and P.V: O rescale when the maximum moved, l and m, then O += P V
+    auto soft_tail = [&](const Soft& sf, f32x16 (&sacc)[2], const char* vt) __attribute__((always_inline)) {
+        const bool grow = sf.grow;
+        const float mu = sf.mu, psum = sf.psum, m_new = sf.m_new;
+        // O and l are still zero while m is -inf: only rows with earlier keys rescale
+        if (__any(grow && m_run != -INFINITY)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        l_run += psum;
+        m_run = m_new;
+
+        // O^T += V^T P^T, four 16-key steps; V^T comes from the transposing LDS read
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int mb = s >> 1, r0 = (s & 1) * 8;
+            // NP bf16 parts of P: part k is the bf16 rounding of P minus parts 0..k-1 (each
+            // difference exact in fp32)
+            Pack8 phi, pmid, plo;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p0 = sacc[mb][r0 + 2 * u], p1 = sacc[mb][r0 + 2 * u + 1];
+                phi.w[u] = cvt_pk_bf16(p0, p1);
+                if (NP >= 2) {
+                    const float e0 = p0 - lo_bf16(phi.w[u]), e1 = p1 - hi_bf16(phi.w[u]);
+                    pmid.w[u] = cvt_pk_bf16(e0, e1);
+                    if (NP == 3) plo.w[u] = cvt_pk_bf16(e0 - lo_bf16(pmid.w[u]), e1 - hi_bf16(pmid.w[u]));
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_ptr)(vt + 16 * s * RB + voff[0][db]));
+                const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16_ptr)(vt + 16 * s * RB + voff[1][db]));
+                Pack8 av;
+                av.w[0] = __builtin_bit_cast(uint2, x0).x;
+                av.w[1] = __builtin_bit_cast(uint2, x0).y;
+                av.w[2] = __builtin_bit_cast(uint2, x1).x;
+                av.w[3] = __builtin_bit_cast(uint2, x1).y;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
+                if (NP >= 2)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
+                if (NP == 3)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
+            }
+        }
+    };
+    auto finish = [&](int tile, f32x16 (&sacc)[2], const char* vt) __attribute__((always_inline)) {
+        const Soft sf = soft_head(tile, sacc, is_full(tile));
+        soft_tail(sf, sacc, vt);
+    };
+    // does the tile meet this wave's key range (and, sparse, its rows' selection)?
+    auto meets = [&](int tile) __attribute__((always_inline)) {
+        const int base = tile * BN;
+        const uint32_t tbit = sparse ? 1u << (tile - t0) : 0u;
+        return base <= w_kmax && base + BN - 1 >= w_kmin && (!sparse || (w_any & tbit));
     };
 
     // one tile: start the next tile's loads into the other stage, compute on this stage,
     // then wait for the loads and meet at the barrier
     auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more,
                     int next) {
-        const int base = tile * BN;
         if (more) issue_tile(next, knext, vnext);
-        // this wave computes only if the tile meets its key range (and, sparse, its rows'
-        // selection)
-        const uint32_t tbit = sparse ? 1u << (tile - t0) : 0u;
-        if (base <= w_kmax && base + BN - 1 >= w_kmin && (!sparse || (w_any & tbit))) {
-            // S^T = K Q^T for two 32-key halves
-            // the two 32-key halves alternate, so each LDS read has two MFMAs to hide behind
+        if (meets(tile)) {
             f32x16 sacc[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
-            // K fragments are read two k-steps ahead of their MFMAs
-            Pack8 ka[2][2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                ka[ks][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks]);
-                ka[ks][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const Pack8 a0 = ka[ks & 1][0], a1 = ka[ks & 1][1];
-                if (ks + 2 < KSTEPS) {
-                    ka[ks & 1][0].u = *reinterpret_cast<const uint4*>(kt + koff[ks + 2]);
-                    ka[ks & 1][1].u = *reinterpret_cast<const uint4*>(kt + 32 * RB + koff[ks + 2]);
-                }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0.v, qreg[ks].v, sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1.v, qreg[ks].v, sacc[1], 0, 0, 0);
-            }
-            // keep the reads two k-steps ahead in the instruction order: 4 reads, then
-            // (2 MFMAs, 2 reads) pairs, then the last 4 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int ks = 0; ks + 2 < KSTEPS; ++ks) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-            // online softmax; t = s * scale * log2(e) is formed inside the exponent's fma
-            const bool full = base >= w_loall && base + BN - 1 <= w_lastall && (!sparse || (w_every & tbit));
-            const bool lsel = !sparse || (eff & tbit);
-            if (!full) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kpos = base + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
-                        if (kpos < lo || kpos > last || !lsel) sacc[mb][r] = -INFINITY;
-                    }
-            }
-            float smax = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[mb][r]);
-            smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-            // lazy maximum: m moves only when the tile's maximum exceeds it by more than
-            // kLazy (log2 units), so p <= 2^kLazy and most tiles need no rescale of O
-            const float m_cand = fmaxf(m_run, smax * cexp);
-            const bool grow = m_cand > m_run + kLazy;
-            const float m_new = grow ? m_cand : m_run;
-            const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-            float psum = 0.f;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][r], cexp, -mu));
-                    sacc[mb][r] = p;
-                    psum += p;
-                }
-            // O and l are still zero while m is -inf: only rows with earlier keys rescale
-            if (__any(grow && m_run != -INFINITY)) {
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mu) : 1.f;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            }
-            l_run += psum;
-            m_run = m_new;
-
-            // O^T += V^T P^T, four 16-key steps; V^T comes from the transposing LDS read
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int mb = s >> 1, r0 = (s & 1) * 8;
-                // NP bf16 parts of P: part k is the bf16 rounding of P minus parts 0..k-1 (each
-                // difference exact in fp32)
-                Pack8 phi, pmid, plo;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float p0 = sacc[mb][r0 + 2 * u], p1 = sacc[mb][r0 + 2 * u + 1];
-                    phi.w[u] = cvt_pk_bf16(p0, p1);
-                    if (NP >= 2) {
-                        const float e0 = p0 - lo_bf16(phi.w[u]), e1 = p1 - hi_bf16(phi.w[u]);
-                        pmid.w[u] = cvt_pk_bf16(e0, e1);
-                        if (NP == 3) plo.w[u] = cvt_pk_bf16(e0 - lo_bf16(pmid.w[u]), e1 - hi_bf16(pmid.w[u]));
-                    }
-                }
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) {
-                    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_v4i16_ptr)(vt + 16 * s * RB + voff[0][db]));
-                    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_v4i16_ptr)(vt + 16 * s * RB + voff[1][db]));
-                    Pack8 av;
-                    av.w[0] = __builtin_bit_cast(uint2, x0).x;
-                    av.w[1] = __builtin_bit_cast(uint2, x0).y;
-                    av.w[2] = __builtin_bit_cast(uint2, x1).x;
-                    av.w[3] = __builtin_bit_cast(uint2, x1).y;
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
-                    if (NP >= 2)
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
-                    if (NP == 3)
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
-                }
-            }
+            scores(kt, sacc);
+            finish(tile, sacc, vt);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    issue_tile(tile_at(0), Ks0, Vs0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int i = 0; i < ntiles; i += 2) {
-        step(tile_at(i), Ks0, Vs0, Ks1, Vs1, i + 1 < ntiles, tile_at(i + 1));
-        if (i + 1 < ntiles) step(tile_at(i + 1), Ks1, Vs1, Ks0, Vs0, i + 2 < ntiles, tile_at(i + 2));
+    bool piped = false;
+    if constexpr (D == 128) piped = !split && !sparse;   // at d = 256 the registers do not fit
+    if (piped) {
+        // Unsplit dense prompts at d = 128 (the long ones): a software-pipelined walk. While tile t's
+        // softmax runs on the VALU, tile t + 1's scores are already on the matrix cores; K is
+        // fetched two tiles ahead and V one. K(t) and V(t) sit in stage (t - t0) & 1. The
+        // arithmetic of every tile is step's, so the bits are the same.
+        f32x16 sa[2], sb[2];
+        // iteration t: K(t + 2) replaces K(t) (its scores were taken last iteration), V(t + 1)
+        // replaces V(t - 1); then scores(t + 1) and finish(t)
+        auto iter = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2], char* kc, const char* kn,
+                        const char* vc, char* vn) __attribute__((always_inline)) {
+            if (t + 2 <= t1) issue_half(t + 2, kc, kg);
+            if (t + 1 <= t1) issue_half(t + 1, vn, vg);
+            if (t + 1 <= t1 && meets(t + 1)) scores(kn, nxt);
+            if (meets(t)) finish(t, cur, vc);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        issue_half(t0, Ks0, kg);
+        issue_half(t0, Vs0, vg);
+        if (t0 + 1 <= t1) issue_half(t0 + 1, Ks1, kg);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (meets(t0)) scores(Ks0, sa);
+        __syncthreads();                    // K(t0) read by every wave before K(t0 + 2) lands
+        for (int t = t0; t <= t1; t += 2) {
+            iter(t, sa, sb, Ks0, Ks1, Vs0, Vs1);
+            if (t + 1 <= t1) iter(t + 1, sb, sa, Ks1, Ks0, Vs1, Vs0);
+        }
+    } else {
+        issue_tile(tile_at(0), Ks0, Vs0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int i = 0; i < ntiles; i += 2) {
+            step(tile_at(i), Ks0, Vs0, Ks1, Vs1, i + 1 < ntiles, tile_at(i + 1));
+            if (i + 1 < ntiles) step(tile_at(i + 1), Ks1, Vs1, Ks0, Vs0, i + 2 < ntiles, tile_at(i + 2));
+        }
     }
 
     // epilogue: O / l, one rounding to bf16; in split mode the chunk's (m, l, O) partial
