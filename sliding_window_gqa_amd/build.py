@@ -3,7 +3,10 @@
     python -m sliding_window_gqa_amd.build
 
 Always recompiles. Packed fp32 VALU instructions are disabled for the device code
-(``-packed-fp32-ops``); the host pass warns that it does not know that feature.
+(``-packed-fp32-ops``); the host pass warns that it does not know that feature. MFMA
+accumulators are kept in VGPRs (``-amdgpu-mfma-vgpr-form``): with the compiler's default
+AGPR form the d = 256 prompt kernel copied its 128 output accumulators between AGPRs and
+VGPRs on every key tile, for the rarely taken rescale of O.
 """
 
 import os
@@ -26,6 +29,7 @@ def compile_flags(extra=()):
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         *extra,
     ]

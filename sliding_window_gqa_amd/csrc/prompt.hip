@@ -419,9 +419,21 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         l_run += psum;
         m_run = m_new;
 
-        // O^T += V^T P^T, four 16-key steps; V^T comes from the transposing LDS read
+        // O^T += V^T P^T, four 16-key steps; V^T comes from the transposing LDS read, one step
+        // ahead of its MFMAs (two register stages of V^T fragments)
+        uint2 vx[2][DBLK][2];
+        auto read_v = [&](int s, uint2 (&dst)[DBLK][2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    dst[db][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_ptr)(vt + 16 * s * RB + voff[u][db])));
+        };
+        read_v(0, vx[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            if (s + 1 < 4) read_v(s + 1, vx[(s + 1) & 1]);
             const int mb = s >> 1, r0 = (s & 1) * 8;
             // NP bf16 parts of P: part k is the bf16 rounding of P minus parts 0..k-1 (each
             // difference exact in fp32)
@@ -438,21 +450,37 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             }
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
-                const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_ptr)(vt + 16 * s * RB + voff[0][db]));
-                const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_ptr)(vt + 16 * s * RB + voff[1][db]));
                 Pack8 av;
-                av.w[0] = __builtin_bit_cast(uint2, x0).x;
-                av.w[1] = __builtin_bit_cast(uint2, x0).y;
-                av.w[2] = __builtin_bit_cast(uint2, x1).x;
-                av.w[3] = __builtin_bit_cast(uint2, x1).y;
+                av.w[0] = vx[s & 1][db][0].x;
+                av.w[1] = vx[s & 1][db][0].y;
+                av.w[2] = vx[s & 1][db][1].x;
+                av.w[3] = vx[s & 1][db][1].y;
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
                 if (NP >= 2)
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
                 if (NP == 3)
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
             }
+        }
+        if constexpr (D == 256) {
+            // keep the order: step 0's reads, then each step's MFMAs with the next step's
+            // reads spread among them
+            // (16 reads a step: two after each MFMA with one part, one with two parts, two
+            // after every three with three parts)
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 2);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const bool more = s + 1 < 4;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                    if (NP == 1 && more) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+                    if (NP >= 2 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+                    if (NP >= 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                    if (NP == 2 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+                    if (NP == 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                    if (NP == 3 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+                }
         }
     };
     auto finish = [&](int tile, f32x16 (&sacc)[2], const char* vt) __attribute__((always_inline)) {
