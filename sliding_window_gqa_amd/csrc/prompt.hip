@@ -26,9 +26,10 @@
 //     by buffer loads with a per-tile descriptor on interior tiles; K fragments are 16-byte
 //     LDS reads, V^T fragments come from the transposing LDS read (ds_read_b64_tr_b16); the
 //     tiles are double buffered, the next tile's loads are in flight while the current tile
-//     computes, and there is one barrier per tile; unsplit dense prompts at d = 128 walk the
-//     tiles software-pipelined (tile t + 1's score MFMAs are issued before tile t's softmax,
-//     K is fetched two tiles ahead and V one), with each tile's arithmetic unchanged;
+//     computes, and there is one barrier per tile; dense prompts at d = 256 and unsplit dense
+//     prompts at d = 128 walk the tiles software-pipelined (tile t + 1's score MFMAs are
+//     issued before tile t's softmax, K is fetched two tiles ahead and V one), with each
+//     tile's arithmetic unchanged;
 //   * the K rows of a tile are fed to the first MFMA in a permuted order so that the S^T
 //     accumulator registers of a lane are, eight at a time, exactly the B operand (P^T) the
 //     P.V MFMA needs for eight consecutive keys: no shuffles between the two products;
@@ -508,10 +509,13 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         __syncthreads();
     };
 
+    // dense prompts at d = 256 (split or not) and unsplit dense prompts at d = 128 (the long
+    // ones) walk their tiles software-pipelined
     bool piped = false;
-    if constexpr (D == 128) piped = !split && !sparse;   // at d = 256 the registers do not fit
+    if constexpr (D == 128) piped = !split && !sparse;
+    if constexpr (D == 256) piped = !sparse;
     if (piped) {
-        // Unsplit dense prompts at d = 128 (the long ones): a software-pipelined walk. While tile t's
+        // A software-pipelined walk. While tile t's
         // softmax runs on the VALU, tile t + 1's scores are already on the matrix cores; K is
         // fetched two tiles ahead and V one. K(t) and V(t) sit in stage (t - t0) & 1. The
         // arithmetic of every tile is step's, so the bits are the same.
