@@ -105,6 +105,13 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, voi
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
 }
 
+// Workgroup barrier that waits for this wave's LDS (and scalar) operations only: global loads
+// still in flight stay in flight across it (__syncthreads would wait for them as well). The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D, int NP>
 __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(PromptArgs a, int nblk) {
     constexpr int KSTEPS = D / 16;
@@ -146,17 +153,22 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     const int head = g * G + pair % G;
     const bool valid = row < a.n;
 
-    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7, loaded before anything else
-    // so that its latency overlaps the key-range set-up
+    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7. At d = 128 (long prompts, where
+    // the set-up below is a negligible part) it is loaded first and waited for at the first
+    // barrier. At d = 256 it is loaded once the row's last key is known, and its loads stay in
+    // flight over the key-range set-up and the first tile loads (the barriers before its
+    // first use wait for LDS operations only); a padding pair then takes row 0's q (each
+    // pair is its own MFMA column and a padding pair's output is never written).
     Pack8 qreg[KSTEPS];
-    {
-        const uint16_t* qp = a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const uint16_t* qp = a.q + (int64_t)(D == 256 && !valid ? 0 : row) * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            if (valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+            if (D == 256 || valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
             else qreg[ks].u = make_uint4(0, 0, 0, 0);
         }
-    }
+    };
+    if constexpr (D == 128) load_q();
 
     const int big = 0x7FFFFFFF;
     int lo = big, last = -1;                // empty range for padding pairs
@@ -165,18 +177,19 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
         last = p;
         if (a.hi) {
-            int hv = a.hi[row];
-            hv = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
-            last = hv;
+            const int hv = a.hi[row];
+            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
         }
     }
+    if constexpr (D == 256) load_q();
     // key range of this wave, the range all its valid pairs see, and the workgroup range
     const int w_kmin = wave_min_i(lo);
     const int w_kmax = wave_max_i(last);
     const int w_loall = wave_max_i(valid ? lo : -1);
     const int w_lastall = wave_min_i(valid ? last : big);
     if (lane == 0) { red_i[0][wave] = w_kmin; red_i[1][wave] = w_kmax; }
-    __syncthreads();
+    if constexpr (D == 256) lds_barrier();
+    else __syncthreads();
     int kmin = red_i[0][0], kmax = red_i[1][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) { kmin = min(kmin, red_i[0][w]); kmax = max(kmax, red_i[1][w]); }
@@ -213,7 +226,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             w_every &= (uint32_t)__shfl_xor((int)w_every, m, 64);
         }
         if (lane == 0) red_sel[wave] = w_any;
-        __syncthreads();
+        if constexpr (D == 256) lds_barrier();
+        else __syncthreads();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) tiles |= red_sel[w];
         if (tiles == 0) return;             // none of the workgroup's rows selected a tile here
@@ -227,16 +241,17 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     };
     const int ntiles = sparse ? __builtin_popcount(tiles) : t1 - t0 + 1;
 
-    // Q^T operand (loaded at the start): a negative scale is carried by q's sign (exact), so
-    // the exponent factor is positive and the row maximum of the raw scores gives the
-    // maximum of the scaled ones.
-    {
+    // First use of the Q^T operand (at d = 256 after the first tile loads are issued): a
+    // negative scale is carried by q's sign (exact), so the exponent factor is positive and
+    // the row maximum of the raw scores gives the maximum of the scaled ones.
+    auto flip_q = [&]() __attribute__((always_inline)) {
         const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             qreg[ks].u.x ^= flip; qreg[ks].u.y ^= flip; qreg[ks].u.z ^= flip; qreg[ks].u.w ^= flip;
         }
-    }
+    };
+    if constexpr (D == 128) flip_q();
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -534,6 +549,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         issue_half(t0, Ks0, kg);
         issue_half(t0, Vs0, vg);
         if (t0 + 1 <= t1) issue_half(t0 + 1, Ks1, kg);
+        if constexpr (D == 256) flip_q();
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (meets(t0)) scores(Ks0, sa);
@@ -544,6 +560,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         }
     } else {
         issue_tile(tile_at(0), Ks0, Vs0);
+        if constexpr (D == 256) flip_q();
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int i = 0; i < ntiles; i += 2) {
