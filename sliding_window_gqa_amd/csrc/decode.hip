@@ -268,8 +268,10 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_ke
 #pragma unroll
         for (int i = 0; i < 16; ++i) B[i] = load_key(un, i);
     };
+    // (The per-unit lambdas are always inlined: at 16 query heads a key head the compiler
+    // otherwise left the head loops rolled and kept the accumulators in scratch memory.)
     // Scores of K unit b: s = scale * (q . k) for every head of the group, into sc.
-    auto consume_k = [&](const Chunk& ch, int b, const uint4 (&B)[16]) {
+    auto consume_k = [&](const Chunk& ch, int b, const uint4 (&B)[16]) __attribute__((always_inline)) {
         const int key = LPK == 32 ? (dl >> 1) : dl;
         const bool writer = LPK == 32 ? (dl & 1) == 0 : true;
         const int kk = run * RUNLEN + 16 * b + key;
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_ke
         }
     };
     float acc[GMAX][8];
-    auto fold_key = [&](const uint4& w, int kk) {
+    auto fold_key = [&](const uint4& w, int kk) __attribute__((always_inline)) {
         const float vf[8] = {lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y),
                              lo_bf16(w.z), hi_bf16(w.z), lo_bf16(w.w), hi_bf16(w.w)};
 #pragma unroll
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_ke
         }
     };
     // P.V of V unit b: fma chains in key order over the run's visible keys
-    auto consume_v = [&](const Chunk& ch, int b, const uint4 (&B)[16]) {
+    auto consume_v = [&](const Chunk& ch, int b, const uint4 (&B)[16]) __attribute__((always_inline)) {
         const int r0 = max(run * RUNLEN, ch.kbase);
         const int r1 = min(run * RUNLEN + RUNLEN, ch.kbase + ch.nk);
         if (r0 == run * RUNLEN && r1 == run * RUNLEN + RUNLEN) {
