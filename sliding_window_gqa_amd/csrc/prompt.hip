@@ -39,6 +39,8 @@
 //   * the workgroup index is remapped so that each XCD (8 on MI355X, workgroups dealt out
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
 //     a key head's K/V stream in that XCD's L2.
+#include <atomic>
+
 #include "wa_common.h"
 #include "rerun_f64.h"
 
@@ -130,12 +132,33 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     __shared__ int red_i[2][kWaves];
     __shared__ uint32_t red_sel[kWaves];
 
-    // XCD-aware remap of the linear workgroup index
+    // XCD-aware remap of the linear workgroup index (the hardware deals ids out to the 8 XCDs
+    // in turn): XCD x takes a contiguous share of the logical ids (key head, block of pairs,
+    // chunk), so one head's K/V stream stays in its L2. With chunk_major the XCD walks its
+    // share chunk-major (every group's first chunk, then every group's second, ...): the
+    // last chunk slots, empty for most groups, are then dispatched last instead of holding
+    // CUs while working workgroups wait (the launcher sets it for dense d = 256 prompts whose
+    // other slots fit in one round of workgroups).
     const int total = gridDim.x;
-    const int L = blockIdx.x;
-    const int xcd = L & 7, idx = L >> 3;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int per = total >> 3, extra = total & 7;
-    const int logical = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + idx;
+    const int share0 = xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per;
+    int logical = share0 + idx;
+    if (D == 256 && a.chunk_major) {
+        const int share1 = share0 + (xcd < extra ? per + 1 : per);
+        const int nc = a.nchunk;
+        int rem = idx;
+        for (int c = 0; c < nc; ++c) {
+            // ids l of the share with l % nc == c: the first one, and how many
+            const int l0 = share0 + (c - share0 % nc + nc) % nc;
+            const int cnt = l0 < share1 ? (share1 - 1 - l0) / nc + 1 : 0;
+            if (rem < cnt) { logical = l0 + rem * nc; break; }
+            rem -= cnt;
+        }
+        // the same for every lane: keep it in a scalar register, so that everything derived
+        // from it (and the branches on it) stays scalar
+        logical = __builtin_amdgcn_readfirstlane(logical);
+    }
     const int cidx = logical % a.nchunk;    // key chunk of the workgroup's range (split mode)
     const int gb = logical / a.nchunk;
     const int g = gb / nblk;                // key head
@@ -795,14 +818,32 @@ __global__ __launch_bounds__(D) void prompt_check_kernel(PromptArgs a) {
     }
 }
 
+// Compute units of the current device, queried once per device (the query costs
+// microseconds of host time, which would land between a caller's events and the launch).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 template <int D>
 hipError_t launch_d(const PromptArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPairs - 1) / kPairs);
     dim3 grid(nblk * a.hkv * a.nchunk);
-    if (a.p_parts == 3) hipLaunchKernelGGL((prompt_kernel<D, 3>), grid, dim3(kThreads), 0, s, a, nblk);
-    else if (a.p_parts == 2) hipLaunchKernelGGL((prompt_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, nblk);
-    else hipLaunchKernelGGL((prompt_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, nblk);
+    // chunk-major dispatch (dense prompts at d = 256, one workgroup a CU) when all but the
+    // last chunk slot of every group fit in one round; measured no faster for sparse prompts,
+    // whose empty slots are not the last ones
+    PromptArgs b = a;
+    b.chunk_major = D == 256 && !a.bm && a.nchunk > 1 && (int64_t)nblk * a.hkv * (a.nchunk - 1) <= cu_count();
+    if (a.p_parts == 3) hipLaunchKernelGGL((prompt_kernel<D, 3>), grid, dim3(kThreads), 0, s, b, nblk);
+    else if (a.p_parts == 2) hipLaunchKernelGGL((prompt_kernel<D, 2>), grid, dim3(kThreads), 0, s, b, nblk);
+    else hipLaunchKernelGGL((prompt_kernel<D, 1>), grid, dim3(kThreads), 0, s, b, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t npairs = (int64_t)a.n * a.hq;
