@@ -4,7 +4,7 @@
 // Method: TensorFold pull request #1257 ("tf_qk_rows_l2"), "What this changes", and the
 // "Exact Numerical Contract" page, "Preparation". For each head of a row at position pos:
 //   WA_PREP_ROPE_L2   r = bf16(rope(x)) with fp32 cos/sin of the fp32 angle
-//                     fl32(fl32(pos) * inv_j), inv_j = fl32(theta^(-2j/R));
+//                     fl32(fl32(pos) * inv_j), inv_j = fl32(theta^(-2j/R)) (inv_j from the host);
 //                     n = bf16(r * (1 / sqrt(sum r^2 + eps)));  q = bf16(qs * n) if qs given
 //   WA_PREP_RMS_ROPE  n = bf16(x * (1 / sqrt(mean x^2 + eps)));
 //                     r = bf16(rope(n)) with bf16(cos), bf16(sin) and fp32 arithmetic
@@ -14,9 +14,10 @@
 // of the row's stream.
 //
 // gfx950 mapping: one workgroup of 256 threads per row. The row's R/2 cos/sin pairs are
-// computed once (float64 pow, cos and sin of the fp32 angle, each rounded once to fp32,
-// i.e. a correctly rounded cosf/sinf) into LDS and shared by all heads. Each wave takes
-// heads h = wave, wave + 4, ... and loads eight of them before computing any: a lane holds
+// computed once (float64 cos and sin of the fp32 angle, each rounded once to fp32, i.e. a
+// correctly rounded cosf/sinf; the inverse frequencies come computed by the host) into LDS
+// and shared by all heads. Each wave takes heads h = wave, wave + 4, ... and loads a batch
+// of them (14 at d = 128, 8 at d = 256) before computing any: a lane holds
 // D/64 consecutive dims (one 4- or 8-byte load), the lane's cos/sin and partner index are
 // fixed for the row, partners of the rotation come through LDS (one row per batch entry,
 // so the eight heads' chains interleave), the sum of squares is a VALU-only wave sum and
@@ -28,7 +29,9 @@ namespace wa {
 namespace {
 
 constexpr int kPrepThreads = 256;
-constexpr int kBatch = 8;              // heads a wave loads before using any
+// heads a wave loads before using any (14 at d = 128: the long prompt's 28 heads a wave in
+// two batches; 8 at d = 256, where the LDS staging row is twice as long)
+template <int D> constexpr int kBatchOf = D == 128 ? 14 : 8;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -64,6 +67,7 @@ template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepArgs a) {
     constexpr int E = D / 64;              // dims per lane
     __shared__ float cs[2][128];           // cos, sin of pair j < R/2 (R <= 256)
+    constexpr int kBatch = kBatchOf<D>;
     __shared__ float xs[kPrepThreads / 64][kBatch][D];
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -92,8 +96,7 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepArgs a) {
     load_batch(wave, w);
     if (a.mode != kPrepCopy) {
         for (int j = tid; j < half; j += kPrepThreads) {
-            const float inv = (float)pow((double)a.theta, -2.0 * (double)j / (double)R);
-            const float ang = (float)pos * inv;
+            const float ang = (float)pos * a.inv[j];
             double sn, cn;
             sincos((double)ang, &sn, &cn);
             cs[0][j] = (float)cn;

@@ -1,5 +1,7 @@
 // C ABI of the wa library: argument checks, workspace sizing and kernel dispatch.
 // The operation and the conventions are documented in include/wa.h.
+#include <cmath>
+
 #include "wa_common.h"
 #include "../../include/wa.h"
 
@@ -228,6 +230,11 @@ int wa_prepare(const wa_prep_t* p,
     if (qs && ((uintptr_t)qs & 3)) return WA_EARG;
     wa::PrepArgs a{};
     a.mode = p->mode; a.rope_dims = p->rope_dims; a.theta = p->theta; a.eps = p->eps;
+    // the inverse frequencies depend on j only: computed once here, in float64 and rounded
+    // once to fp32, instead of on every row of the kernel
+    if (p->mode != WA_PREP_COPY)
+        for (int j = 0; j < p->rope_dims / 2; ++j)
+            a.inv[j] = (float)std::pow((double)p->theta, -2.0 * (double)j / (double)p->rope_dims);
     a.x = x; a.x_srow = x_srow; a.x_shead = x_shead;
     a.pos_of_row = pos_of_row; a.qs = qs;
     a.rows = rows; a.heads = heads; a.d = d;

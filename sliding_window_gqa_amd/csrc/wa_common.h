@@ -82,6 +82,7 @@ constexpr int kPromptChunk = 384;
 constexpr int kPrepCopy = 0, kPrepRopeL2 = 1, kPrepRmsRope = 2;
 struct PrepArgs {
     int32_t mode, rope_dims; float theta, eps;
+    float inv[128];               // fl32(theta^(-2j / rope_dims)), j < rope_dims / 2 (host, float64 pow)
     const uint16_t* x; int64_t x_srow, x_shead;
     const int32_t* pos_of_row; const float* qs;
     int32_t rows, heads, d;
