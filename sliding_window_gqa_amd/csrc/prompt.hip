@@ -38,7 +38,11 @@
 //     exceeds it by more than 2^8 in probability), so the O rescale runs on few tiles;
 //   * the workgroup index is remapped so that each XCD (8 on MI355X, workgroups dealt out
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
-//     a key head's K/V stream in that XCD's L2.
+//     a key head's K/V stream in that XCD's L2 (chunk-major inside the range when the
+//     launcher asks for it);
+//   * at d = 256 (one wave a SIMD) the MFMA accumulators stay in VGPRs (the library is built
+//     with -amdgpu-mfma-vgpr-form), the V^T fragments of the next 16-key step are read while
+//     the current step's MFMAs run, and the Q loads stay in flight across the set-up.
 #include <atomic>
 
 #include "wa_common.h"
