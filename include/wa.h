@@ -158,7 +158,9 @@ size_t wa_prompt_workspace(const wa_window_t* w, int32_t n, int32_t hq, int32_t 
  * absolute chunk and tile grid, not on how the prompt is cut into calls.
  * The ring must hold keys [min lo_i, p0 + n - 1] without two of them sharing a slot:
  * ring >= p0 + n - max(0, p0 - window + 1) (window > 0) or ring >= p0 + n (window == 0),
- * else WA_ERANGE. hi values out of range are clamped into [p0 + i, p0 + n - 1].
+ * else WA_ERANGE. A 64-key tile of a key head is addressed with 32-bit byte offsets:
+ * 63 * kv_sslot * 2 + 2 * d >= 2^31 - 1 is also WA_ERANGE.
+ * hi values out of range are clamped into [p0 + i, p0 + n - 1].
  * w->p32 selects P's representation (WA_P_*; another value is WA_EUNSUPPORTED).
  * Errors: WA_EARG, WA_EUNSUPPORTED, WA_ERANGE, WA_EWORKSPACE, WA_EHIP.
  */

@@ -66,6 +66,21 @@ def accept(out_bits, x, S, e_p, tier="G"):
     return ok
 
 
+# The literal one-ulp rule. A value y with |y - x| <= 2**-9 |x| rounds to a bf16 within one
+# step of bf16(x), in every binade and at binade edges: the bf16 spacing s next to x is at
+# least 2**-8 |x| (2**-133 among subnormals), and from anywhere in the rounding cell of
+# r = bf16(x) a move of at most s / 2 ends at or before the neighbour's value. An output
+# outside {r and its two neighbours} therefore carries an error above 2**-9 |x|; with the
+# error at most (e_P + 2**-16) S (the S term of the half-width), that needs
+# |x| < 2**9 (e_P + 2**-16) S: a cancelling output, far below the scale S of its terms.
+LITERAL_STEP = 2.0 ** -9
+
+
+def literal_bound(e_p):
+    """Largest |x| / S an output outside the one-step set can have under the S allowance."""
+    return (e_p + 2.0 ** -16) / LITERAL_STEP
+
+
 def literal_stats(out_bits, x):
     """Counts for the literal one-ulp statistic: equal to bf16(x), and within one bf16 step."""
     out = np.asarray(out_bits).astype(np.uint16)
@@ -79,10 +94,30 @@ def literal_stats(out_bits, x):
     return {"n": int(out.size), "equal": int(eq.sum()), "within_1ulp": int(near.sum())}
 
 
+def literal_outside(out_bits, x, S):
+    """The outputs outside the one-step set: their count and the largest |x| / S among them
+    (0 when there are none)."""
+    out = np.asarray(out_bits).astype(np.uint16)
+    x = np.asarray(x, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    r = bf16.to_bf16_bits(x)
+    eq = (out == r) | (np.isnan(x) & bf16.is_nan(out))
+    near = eq | (np.isfinite(x) & (np.abs(bf16.order_key(out) - bf16.order_key(r)) <= 1)
+                 & ~bf16.is_nan(out))
+    far = ~near
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(S > 0, np.abs(x) / np.where(S > 0, S, 1.0), np.inf)
+    worst = float(ratio[far].max()) if far.any() else 0.0
+    return int(far.sum()), worst
+
+
 def report(out_bits, x, S, e_p):
-    """Summary dict used by tests and the bench: gate counts and the literal statistic."""
+    """Summary dict used by tests and the bench: gate counts and the literal statistic
+    (equal to bf16(x), within one step, outside, and the largest |x| / S outside)."""
     g = accept(out_bits, x, S, e_p, "G")
     s = accept(out_bits, x, S, e_p, "S")
     d = literal_stats(out_bits, x)
-    d.update({"tier_G_fail": int((~g).sum()), "tier_S_fail": int((~s).sum())})
+    outside, worst = literal_outside(out_bits, x, S)
+    d.update({"outside": outside, "worst_x_over_S": worst,
+              "tier_G_fail": int((~g).sum()), "tier_S_fail": int((~s).sum())})
     return d

@@ -1,0 +1,26 @@
+// One instantiation of the prompt kernel (prompt_impl.h): head dim WA_INST_D with P in
+// WA_INST_NP bf16 parts; with WA_INST_POST also the merge and check kernels at that head dim.
+// The build compiles this file once per variant the launcher in prompt.hip calls, so that
+// they compile in parallel.
+#include "prompt_impl.h"
+
+#if !defined(WA_INST_D) || !defined(WA_INST_NP) || !defined(WA_INST_POST)
+#error "prompt_inst.hip is compiled with -DWA_INST_D=.. -DWA_INST_NP=.. -DWA_INST_POST=0|1"
+#endif
+
+#define WA_CAT3(a, b, c) a##b##_##c
+#define WA_MAIN(d, np) WA_CAT3(launch_prompt_main_, d, np)
+#define WA_CAT2(a, b) a##b
+#define WA_POST(d) WA_CAT2(launch_prompt_post_, d)
+
+namespace wa {
+
+hipError_t WA_MAIN(WA_INST_D, WA_INST_NP)(const PromptArgs& b, int nblk, unsigned grid, hipStream_t s) {
+    return launch_main<WA_INST_D, WA_INST_NP>(b, nblk, grid, s);
+}
+
+#if WA_INST_POST
+hipError_t WA_POST(WA_INST_D)(const PromptArgs& a, hipStream_t s) { return launch_post<WA_INST_D>(a, s); }
+#endif
+
+}  // namespace wa

@@ -17,6 +17,12 @@ bool window_ok(const wa_window_t* w) {
     return w && w->window >= 0 && w->ring > 0 && w->scale == w->scale;
 }
 
+// The prompt kernel addresses one 64-key tile of K or V with 32-bit byte offsets from the
+// tile's first slot: 63 slot strides plus one row must stay below 2^31 bytes.
+bool prompt_extent_ok(int64_t kv_sslot, int d) {
+    return 63 * kv_sslot * 2 + 2 * (int64_t)d < 0x7FFFFFFF;
+}
+
 int chunk_capacity(const wa_window_t* w, int32_t max_pos) {
     if (!window_ok(w) || max_pos < 0) return 0;
     if (w->window > 0) return (w->window - 1 + wa::kChunk - 1) / wa::kChunk + 1;
@@ -125,6 +131,7 @@ int wa_prompt(const wa_window_t* w,
     if ((int64_t)p0 + n > 0x7FFFFFFF || (int64_t)n + w->window > 0x3FFFFFFF) return WA_ERANGE;
     const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
     if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
+    if (!prompt_extent_ok(kv_sslot, d)) return WA_ERANGE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
     if ((q_srow | q_shead | kv_sslot | kv_shead) & 7) return WA_EARG;
     if (((uintptr_t)out & 7) || ((o_srow | o_shead) & 3)) return WA_EARG;
@@ -180,6 +187,7 @@ int wa_prompt_sparse(const wa_window_t* w,
     if ((int64_t)p0 + n > 0x7FFFFFFF || (int64_t)n + w->window > 0x3FFFFFFF) return WA_ERANGE;
     const int64_t first = w->window > 0 ? (int64_t)(p0 - w->window + 1 > 0 ? p0 - w->window + 1 : 0) : 0;
     if ((int64_t)w->ring < (int64_t)p0 + n - first) return WA_ERANGE;
+    if (!prompt_extent_ok(kv_sslot, d)) return WA_ERANGE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return WA_EARG;
     if ((q_srow | q_shead | kv_sslot | kv_shead) & 7) return WA_EARG;
     if (((uintptr_t)out & 7) || ((o_srow | o_shead) & 3)) return WA_EARG;

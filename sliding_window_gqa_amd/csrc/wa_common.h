@@ -78,6 +78,9 @@ __device__ __forceinline__ bool block_selected(const uint32_t* row_mask, int wor
 // 512-row chunk then fills the GPU in one round of workgroups)
 constexpr int kPromptChunk = 384;
 
+// (row, query head) pairs per workgroup of the prompt kernel (4 waves of 32)
+constexpr int kPromptPairs = 128;
+
 // q/k row preparation (modes as in wa.h)
 constexpr int kPrepCopy = 0, kPrepRopeL2 = 1, kPrepRmsRope = 2;
 struct PrepArgs {

@@ -1,6 +1,8 @@
 """Helpers shared by the GPU tests: move seeded inputs to the device, call the library
 through its binding, and compare with the float64 oracle."""
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -75,17 +77,33 @@ def oracle_prompt(case, rows=None):
                          hi=case.hi, rows=rows)
 
 
+def _record(label, e_p, rep):
+    """Append one case's counts to the JSON-lines file named by WA_PARITY_LOG, if set."""
+    path = os.environ.get("WA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": label, "e_P": e_p, **rep}) + "\n")
+
+
 def compare(out, x, S, e_p, label):
-    """Gate: every output inside its tier-G interval. Logs the literal statistic."""
+    """Gate: every output inside its tier-G interval. Where P is fp32 to 2**-16 or better
+    (e_P <= 2**-16), also the literal one-ulp rule: every output outside {bf16(x) and its two
+    neighbours} must be a cancelling one, |x| / S < check.literal_bound(e_P). The counts
+    (equal, within one step, outside, worst |x| / S outside) are logged and recorded."""
     rep = check.report(out, x, S, e_p)
-    log(f"[{label}] n={rep['n']} equal={rep['equal']} within1ulp={rep['within_1ulp']} "
-        f"tierG_fail={rep['tier_G_fail']} tierS_fail={rep['tier_S_fail']}")
+    msg = (f"[{label}] n={rep['n']} equal={rep['equal']} within1ulp={rep['within_1ulp']} "
+           f"outside={rep['outside']} worst|x|/S={rep['worst_x_over_S']:.3g} "
+           f"tierG_fail={rep['tier_G_fail']} tierS_fail={rep['tier_S_fail']}")
+    log(msg)
+    _record(label, e_p, rep)
     ok = check.accept(out, x, S, e_p, "G")
     if not ok.all():
         bad = np.argwhere(~ok)[:10]
         for idx in bad:
             t = tuple(idx)
             log(f"  fail at {t}: out=0x{int(out[t]):04x} x={x[t]!r} S={S[t]!r}")
+    if e_p <= check.E_P_P32:
+        assert rep["worst_x_over_S"] < check.literal_bound(e_p), "literal rule: " + msg
     return rep, ok
 
 

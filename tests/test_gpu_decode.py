@@ -245,7 +245,7 @@ def test_decode_nonfinite_classes():
     x, S, _ = gu.oracle_decode(c)
     assert check.accept(out, x, S, E_P).all()
     assert np.isinf(x[2, 0:2, 9]).all() and np.isfinite(x[[0, 1, 3]]).all()
-    # +inf and -inf in one column
+    # opposite infinities sharing one value column
     c = _nf_case()
     c.v[0, 290, 1, 4] = PINF
     c.v[0, 291, 1, 4] = NINF
@@ -270,8 +270,9 @@ def test_decode_inf_at_negligible_key():
 
 def test_decode_nonfinite_whole_rows():
     """Non-finite plants in a batch large enough for the whole-row kernel (64 rows x 8 key
-    heads, one stream per row): NaN query, visible NaN key, +inf value, +inf and -inf in one
-    column, and +inf at a key whose float64 weight is e^-200 next to a score-200 key. Every
+    heads, one stream per row): NaN query, visible NaN key, +inf value, opposite infinities in
+    the same value column, and an infinite value on a key scoring 200 below the row's peak
+    (float64 weight e^-200, fp32 weight 0). Every
     output must be in its interval, with float64's class, and each planted row must have the
     bits it has when computed alone (chunk-partial kernel + merge)."""
     NAN, PINF, NINF = 0x7FC0, 0x7F80, 0xFF80

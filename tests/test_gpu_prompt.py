@@ -3,8 +3,8 @@
 Gate: every bf16 output inside its tier-G interval (oracle.check) with e_P = 2**-16 for p32,
 2**-8 for P as one bf16 and 0 for P as three bf16 parts (which must also meet the strict
 interval of fp32 P). Masks are pinned by peaked-edge probes; chunk invariance
-(TensorFold pull request #1123, "Receipt", exactness bullet: a prompt chunk split in two
-gives every row's bits) and repeatability by byte equality.
+(TensorFold pull request #1123, "Receipt", exactness bullet: cutting a prompt chunk into two
+calls must leave each row's bits unchanged) and repeatability by byte equality.
 """
 
 import numpy as np
@@ -124,6 +124,25 @@ def test_prompt_shapes(n, hq, hkv, d, p0, win, ring, p32, span):
     _gate(case, f"prompt shape n{n} {hq}/{hkv}x{d} p0={p0} win{win} ring{ring}")
 
 
+SHORT_RINGS = [
+    # n, hq, hkv, d, p0, win, ring, p32: rings shorter than one 64-key tile, so that an
+    # edge tile's keys wrap around the ring several times (window 8 over 11 slots, ...)
+    (4, 2, 1, 256, 100, 8, 11, True),
+    (4, 2, 1, 128, 100, 8, 11, False),
+    (30, 4, 2, 256, 500, 20, 49, THREE),
+    (12, 2, 2, 128, 3, 0, 15, True),
+    (9, 3, 1, 256, 61, 5, 13, False),
+]
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,p0,win,ring,p32", SHORT_RINGS)
+def test_prompt_short_rings(n, hq, hkv, d, p0, win, ring, p32):
+    """Keys of a ring shorter than a tile come from slot j mod ring on every tile."""
+    case = workloads.prompt_case("short ring", n, hq, hkv, d, p0, win, ring, seed=3 * n + ring,
+                                 p32=p32, peak_every=2)
+    _gate(case, f"short ring n{n} {hq}/{hkv}x{d} p0={p0} win{win} ring{ring}")
+
+
 def _split_check(case, cuts):
     full = gu.run_prompt(case)
     for cut in cuts:
@@ -134,8 +153,9 @@ def _split_check(case, cuts):
 
 
 def test_prompt_chunk_invariance_and_repeat():
-    """A prompt split in two gives every row's bits. A chunk must hold an image's rows whole
-    (hi[i] < p0 + n), so the image-span workload is cut only outside its span (rows 40..300);
+    """Cutting the prompt into two calls leaves each row's bits unchanged. A chunk must hold
+    an image's rows whole (hi[i] < p0 + n), so the image-span workload is cut only outside
+    its span (rows 40..300);
     the same shape without an image span, and the causal 31B workload, are cut anywhere."""
     case = workloads.prompt_12b()
     full = _split_check(case, (1, 17, 39, 40, 301, 302, 400, 511))
@@ -250,6 +270,7 @@ def test_prompt_inf_value_unseen_by_tile_neighbours(win, p32):
         out = gu.run_prompt(case)
         x, S, _ = gu.oracle_prompt(case)
         assert np.isinf(x[:, 0:2, 3]).all()
+        assert check.accept(out, x, S, e_p(p32)).all()
         case.v[240, 0, 3] = case.v[241, 0, 3]
         case.v[349, 0, 3] = 0x7F80            # the last key: only rows 4..49 see it
         out = gu.run_prompt(case)

@@ -72,6 +72,17 @@ def test_every_block_selected_gives_wa_prompt_bits():
         assert np.array_equal(gu.run_sparse(case), dense), p32
 
 
+def test_short_ring_blocks():
+    """A ring shorter than one block: keys 53..67 over 15 slots, rows selecting block 0 or
+    both blocks, against the oracle."""
+    case = workloads.prompt_case("sparse short ring", 8, 2, 1, 256, 60, 8, 15, seed=12, p32=2,
+                                 peak_every=2)
+    case.masks = np.zeros((case.n, 1), np.uint32)
+    case.masks[0::2, 0] = 0x1
+    case.masks[1::2, 0] = 0x3
+    _gate(case, "sparse short ring")
+
+
 def test_rows_independent_of_the_other_rows_and_cuts():
     case = workloads.sparse_prompt()
     full = gu.run_sparse(case)

@@ -207,7 +207,7 @@ def test_invariants_batch_stream_cache_length_chunking():
     a = attend.decode(q[:1], lin_k[:, :50], lin_v[:, :50], [0], [30], 0, 50, 1.0)[2]
     b = attend.decode(q[:1], lin_k, lin_v, [0], [30], 0, 16 * 50, 1.0)[2]
     assert np.array_equal(a, b)
-    # a prompt split in two gives every row's bits
+    # cutting a prompt into two calls leaves each row's bits unchanged
     n, p0 = 12, 30
     qp = rand_bf16(rng, (n, Hq, d))
     whole = attend.prompt(qp, kc[0], vc[0], p0, win, ring, 1.0)[2]

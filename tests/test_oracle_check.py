@@ -61,6 +61,46 @@ def test_literal_stats_counts():
     assert st == {"n": 4, "equal": 2, "within_1ulp": 3}
 
 
+def _steps(a_bits, b_bits):
+    return np.abs(bf16.order_key(a_bits) - bf16.order_key(b_bits))
+
+
+def test_literal_step_lemma():
+    """|y - x| <= 2**-9 |x| keeps bf16(y) within one step of bf16(x): across binades, at
+    powers of two from both sides, on rounding midpoints and among subnormals; a relative
+    error of 2**-7 does not (so the claim has content)."""
+    rng = np.random.default_rng(11)
+    e = rng.integers(-140, 120, size=200000)
+    m = rng.uniform(1.0, 2.0, size=e.size)
+    x = np.ldexp(m, e) * rng.choice([-1.0, 1.0], size=e.size)
+    # exact powers of two, their neighbours and the rounding midpoints around them
+    p2 = np.ldexp(1.0, np.arange(-135, 100))
+    x = np.concatenate([x, p2, p2 * (1 - 2.0 ** -9), p2 * (1 + 2.0 ** -8), p2 * (1 - 2.0 ** -8)])
+    for t in (-1.0, -0.5, 0.5, 1.0):
+        y = x + t * check.LITERAL_STEP * np.abs(x)
+        assert _steps(bf16.to_bf16_bits(y), bf16.to_bf16_bits(x)).max() <= 1, t
+    y = x + 2.0 ** -7 * np.abs(x)
+    assert _steps(bf16.to_bf16_bits(y), bf16.to_bf16_bits(x)).max() >= 2
+
+
+def test_literal_outside_report():
+    x = np.array([1.0, 1.0, 1.0, -3.0, 0.25])
+    S = np.array([1.0, 2.0 ** 8, 4.0, 3.0, 1.0])
+    # 1.0 + 3 steps (|x|/S = 2**-8), one step, equal, -3 + 2 steps (|x|/S = 1), equal
+    out = np.array([0x3F83, 0x3F81, 0x3F80, 0xC042, 0x3E80], np.uint16)
+    n_out, worst = check.literal_outside(out, x, S)
+    assert (n_out, worst) == (2, 1.0)
+    n_out, worst = check.literal_outside(out[:3], x[:3], S[:3])
+    assert (n_out, worst) == (1, 1.0)
+    n_out, worst = check.literal_outside(out[1:3], x[1:3], S[1:3])
+    assert (n_out, worst) == (0, 0.0)
+    rep = check.report(out, x, S, check.E_P_FP32)
+    assert (rep["outside"], rep["equal"], rep["within_1ulp"]) == (2, 2, 3)
+    # the bound: 2**9 (e_P + 2**-16)
+    assert check.literal_bound(check.E_P_FP32) == 2.0 ** -7
+    assert check.literal_bound(check.E_P_P32) == 2.0 ** -6
+
+
 # ---- float32 emulation of chunked decode (CPU test code, numpy float32 steps) -----------
 
 def emulate_decode(q, kc, vc, stream, pos, win, ring, chunk=256, early=0, no_rescale=False,

@@ -2,8 +2,9 @@
 
 Sources: TensorFold pull request #1257, "What this changes" (rotate-half RoPE on the bf16
 projection rows with the fp32 angle fl32(pos * inv), inv = fp32 1/theta^(2j/d); L2 with eps
-on the sum; q scaled by an fp32 vector; rounding points: the rotated head, the normalized
-head, q after the scale; the two planted controls that drop a rounding point) and the
+on the sum; q scaled by an fp32 vector; bf16 roundings after the rotation, after the
+normalisation and after the q scale; the two planted controls that skip one of those
+roundings) and the
 "Exact Numerical Contract" page, "Preparation" (per-head RMSNorm, eps 1e-5, fp32, rounded
 to bf16; split-half RoPE on dims 0-95 with bf16 coefficients and fp32 arithmetic, rounded
 to bf16; dims 96-127 unrotated).
