@@ -81,7 +81,8 @@ enum {
     WA_EUNSUPPORTED = -2,  /* head dim other than 128/256, hq % hkv != 0, group > 16 */
     WA_ERANGE = -3,        /* window/ring inconsistent with the positions the call can reach */
     WA_EWORKSPACE = -4,    /* decode workspace missing or smaller than wa_decode_workspace() */
-    WA_EHIP = -5           /* a kernel launch failed (hipGetLastError after the launch) */
+    WA_EHIP = -5,          /* a kernel launch failed (hipGetLastError after the launch) */
+    WA_ESCRATCH = -6       /* wa_decode_noalloc: the call needs more than its static scratch */
 };
 
 /* Most chunks a decode row can span: window > 0: (window - 1 + 255) / 256 + 1;
@@ -120,6 +121,28 @@ int wa_decode(const wa_window_t* w,
               int32_t rows, int32_t hq, int32_t hkv, int32_t d,
               void* ws, size_t ws_bytes,
               uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
+
+/*
+ * Decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): wa_decode with the same arguments except
+ * the workspace, whose role a static device array of WA_NOALLOC_SCRATCH_BYTES (8 MiB) takes.
+ * Each GPU the library runs on holds its own copy of that array from the first call on that
+ * device until the process ends; the call allocates and frees nothing. Results are wa_decode's
+ * bits. A call whose wa_decode_workspace() size exceeds WA_NOALLOC_SCRATCH_BYTES returns
+ * WA_ESCRATCH and launches nothing (8 MiB holds the partials of, e.g., 101 rows of 16 heads x
+ * 256 over 5 chunks). Every call on one GPU uses that GPU's one array and leaves its partials
+ * there: calls that may overlap on one GPU (other streams, other host threads) race and must
+ * be serialised by the caller. Other errors as wa_decode (WA_EHIP also if the array's device
+ * address cannot be queried).
+ */
+#define WA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int wa_decode_noalloc(const wa_window_t* w,
+                      const uint16_t* q, int64_t q_srow, int64_t q_shead,
+                      const uint16_t* k, const uint16_t* v,
+                      int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+                      const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+                      int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+                      uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream);
 
 /*
  * Merge of decode partials (the second half of wa_decode, exposed so that partials made

@@ -58,6 +58,9 @@ SIGNATURES = {
     "wa_decode": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I32,
                                  _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ,
                                  _P, _I64, _I64, _P]),
+    "wa_decode_noalloc": (ctypes.c_int, [_WP, _P, _I64, _I64, _P, _P, _I64, _I64, _I64, _I32,
+                                         _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                         _P, _I64, _I64, _P]),
     "wa_merge": (ctypes.c_int, [_WP, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                 _P, _I64, _I64, _P]),
     "wa_prompt_workspace": (_SZ, [_WP, _I32, _I32, _I32]),
@@ -144,6 +147,31 @@ def decode(q, k, v, stream_of_row, pos_of_row, win, ring, scale=1.0, max_pos=Non
                            out.data_ptr(), out.stride(0), out.stride(1), _stream()))
     return out
 
+
+
+def decode_noalloc(q, k, v, stream_of_row, pos_of_row, win, ring, scale=1.0, max_pos=None,
+                   out=None):
+    """decode() through wa_decode_noalloc: the library's static scratch instead of a
+    workspace (pass ``out`` to allocate nothing at all). Same arguments and result."""
+    _bf16(q, "q"); _bf16(k, "k"); _bf16(v, "v")
+    _i32(stream_of_row, "stream_of_row"); _i32(pos_of_row, "pos_of_row")
+    if k.shape != v.shape or k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must share one [streams, ring, Hkv, d] layout")
+    rows, hq, d = q.shape
+    streams, ring_k, hkv, dk = k.shape
+    if dk != d or ring_k != ring:
+        raise ValueError("k/v shape does not match q or the ring length")
+    if max_pos is None:
+        max_pos = INT32_MAX if win > 0 else ring - 1
+    w = window(win, ring, scale)
+    if out is None:
+        out = torch.empty((rows, hq, d), dtype=torch.bfloat16, device=q.device)
+    _check(lib().wa_decode_noalloc(ctypes.byref(w), q.data_ptr(), q.stride(0), q.stride(1),
+                                   k.data_ptr(), v.data_ptr(), k.stride(0), k.stride(1),
+                                   k.stride(2), streams, stream_of_row.data_ptr(),
+                                   pos_of_row.data_ptr(), max_pos, rows, hq, hkv, d,
+                                   out.data_ptr(), out.stride(0), out.stride(1), _stream()))
+    return out
 
 def merge(m, l, o, pos_of_row, win, ring, out=None):
     """Merge decode partials m, l [rows, Hq, C] and o [rows, Hq, C, d] (fp32, CUDA)."""

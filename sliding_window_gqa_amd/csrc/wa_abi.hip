@@ -1,6 +1,7 @@
 // C ABI of the wa library: argument checks, workspace sizing and kernel dispatch.
 // The operation and the conventions are documented in include/wa.h.
 #include <cmath>
+#include <mutex>
 
 #include "wa_common.h"
 #include "../../include/wa.h"
@@ -47,14 +48,19 @@ size_t wa_decode_workspace(int32_t rows, int32_t hq, int32_t d, const wa_window_
     return (2 * cells2 + cells * (size_t)d) * sizeof(float);
 }
 
-int wa_decode(const wa_window_t* w,
-              const uint16_t* q, int64_t q_srow, int64_t q_shead,
-              const uint16_t* k, const uint16_t* v,
-              int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
-              const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
-              int32_t rows, int32_t hq, int32_t hkv, int32_t d,
-              void* ws, size_t ws_bytes,
-              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// wa_decode's checks and launch; ws is the caller's workspace or this device's scratch
+int decode_call(const wa_window_t* w,
+                const uint16_t* q, int64_t q_srow, int64_t q_shead,
+                const uint16_t* k, const uint16_t* v,
+                int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+                const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+                int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+                void* ws, size_t ws_bytes,
+                uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
     if (!w || !q || !k || !v || !stream_of_row || !pos_of_row || !out) return WA_EARG;
     if (rows <= 0 || streams <= 0 || max_pos < 0) return WA_EARG;
     if (q_srow < 0 || q_shead < 0 || kv_sstream < 0 || kv_sslot < 0 || kv_shead < 0 ||
@@ -87,6 +93,64 @@ int wa_decode(const wa_window_t* w,
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (wa::launch_decode(a, s) != hipSuccess) return WA_EHIP;
     return WA_OK;
+}
+
+// Scratch of wa_decode_noalloc: a static device array (each GPU the library runs on holds its
+// own copy, for the life of the process). Host code never passes the array's name to a
+// kernel (on the host it is only a handle); it passes the device address that
+// hipGetSymbolAddress gives, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[WA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// this device's scratch address, or nullptr if the device or the symbol query fails
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_dev[dev] = p;
+    }
+    return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int wa_decode(const wa_window_t* w,
+              const uint16_t* q, int64_t q_srow, int64_t q_shead,
+              const uint16_t* k, const uint16_t* v,
+              int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+              const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+              int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+              void* ws, size_t ws_bytes,
+              uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    return decode_call(w, q, q_srow, q_shead, k, v, kv_sstream, kv_sslot, kv_shead, streams,
+                       stream_of_row, pos_of_row, max_pos, rows, hq, hkv, d, ws, ws_bytes,
+                       out, o_srow, o_shead, stream);
+}
+
+int wa_decode_noalloc(const wa_window_t* w,
+                      const uint16_t* q, int64_t q_srow, int64_t q_shead,
+                      const uint16_t* k, const uint16_t* v,
+                      int64_t kv_sstream, int64_t kv_sslot, int64_t kv_shead, int32_t streams,
+                      const int32_t* stream_of_row, const int32_t* pos_of_row, int32_t max_pos,
+                      int32_t rows, int32_t hq, int32_t hkv, int32_t d,
+                      uint16_t* out, int64_t o_srow, int64_t o_shead, void* stream) {
+    const size_t need = wa_decode_workspace(rows, hq, d, w, max_pos);
+    if (need > WA_NOALLOC_SCRATCH_BYTES) return WA_ESCRATCH;
+    void* ws = need ? scratch_ptr() : nullptr;
+    if (need && !ws) return WA_EHIP;
+    // every partial the merge reads is written by the chunk kernel of the same call first,
+    // so the scratch needs no clearing between calls
+    return decode_call(w, q, q_srow, q_shead, k, v, kv_sstream, kv_sslot, kv_shead, streams,
+                       stream_of_row, pos_of_row, max_pos, rows, hq, hkv, d, ws,
+                       WA_NOALLOC_SCRATCH_BYTES, out, o_srow, o_shead, stream);
 }
 
 int wa_merge(const wa_window_t* w, const float* m, const float* l, const float* o,
@@ -260,6 +324,7 @@ const char* wa_status_string(int status) {
         case WA_ERANGE: return "window or ring inconsistent with the positions";
         case WA_EWORKSPACE: return "workspace missing or too small";
         case WA_EHIP: return "kernel launch failed";
+        case WA_ESCRATCH: return "call needs more than wa_decode_noalloc's static scratch";
         default: return "unknown status";
     }
 }
