@@ -77,19 +77,42 @@ SIGNATURES = {
 }
 
 
+def load_library(path):
+    """Load a build of the library at ``path`` with the C signatures set (the product library,
+    or another build of the same sources)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m sliding_window_gqa_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     """Load libwa.so once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sliding_window_gqa_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+class using:
+    """Context in which the binding's calls go to another build of the library (``L`` from
+    load_library), e.g. a build with a planted mistake that a test must see fail."""
+
+    def __init__(self, L):
+        self.L = L
+
+    def __enter__(self):
+        global _lib
+        self.prev, _lib = _lib, self.L
+        return self.L
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
 
 
 def _check(status):

@@ -88,6 +88,19 @@ __device__ __forceinline__ int sigma(int i) {
     return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
+// Both lane halves of a pair combined, on every lane, without an LDS round trip: the
+// half-swap (v_permlane32_swap) leaves lanes l and l ^ 32 holding each other's value in one of
+// its two results, and max / sum of the two results is the pair's (the same order of operands
+// on both halves, so both lanes get the same bits).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m, 64));
@@ -434,7 +447,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[mb][r]);
-        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+        smax = pair_max(smax);
         // lazy maximum: m moves only when the tile's maximum exceeds it by more than
         // kLazy (log2 units), so p <= 2^kLazy and most tiles need no rescale of O
         Soft sf;
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     }
 
     // epilogue: O / l, one rounding to bf16; in split mode the chunk's (m, l, O) partial
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = pair_sum(l_run);
     if (split) {
         // the partial of a chunk holding at least one of the row's keys (sparse: of its
         // selected blocks); the merge reads exactly these
