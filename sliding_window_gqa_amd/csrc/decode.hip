@@ -110,7 +110,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
         for (int e = 0; e < DL; ++e) num[e] = 0.f;
         for (int cb = 0; cb < n; cb += 64) {
             const bool in = cb + lane < n;
-            const float ac = expf((cb == 0 ? m0 : (in ? a.m[pi + cb + lane] : -INFINITY)) - M);
+            const float ac = WA_CONTROL == 3 ? (in ? 1.f : 0.f)
+                                             : expf((cb == 0 ? m0 : (in ? a.m[pi + cb + lane] : -INFINITY)) - M);
             const float lc = cb == 0 ? l0 : (in ? a.l[pi + cb + lane] : 0.f);
             const int ce = min(n - cb, 64);
             // eight chunks' o loads in flight at a time, then their fmas in chunk order
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
         bool bad = false;
 #pragma unroll
         for (int e = 0; e < DL; ++e) {
-            const uint32_t b = f32_to_bf16_rne(num[e] / den);
+            const uint32_t b = merge_round(num[e] / den);
             orow[DL * lane + e] = (uint16_t)b;
             bad = bad || bf16_nonfinite((uint16_t)b);
         }

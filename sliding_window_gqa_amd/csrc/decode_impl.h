@@ -69,10 +69,16 @@ __device__ __forceinline__ RowSpan row_span(const int32_t* pos_of_row, int r, in
     int p = pos_of_row[r];
     p = p < 0 ? 0 : (p > max_pos ? max_pos : p);
     s.pos = p;
-    s.lo = window > 0 ? max(0, p - window + 1) : 0;
+    s.lo = window > 0 ? max(0, p - window + 1 - (WA_CONTROL == 1)) : 0;
     s.c_lo = s.lo / kChunk;
     s.c_hi = p / kChunk;
     return s;
+}
+
+// The merge's final rounding (nearest-even; toward zero in control build 4).
+__device__ __forceinline__ uint32_t merge_round(float x) {
+    if constexpr (WA_CONTROL == 4) return (x != x) ? 0x7FC0u : (__float_as_uint(x) >> 16);
+    return f32_to_bf16_rne(x);
 }
 
 // Linear workgroup id -> logical id such that each XCD (8 on MI355X, ids dealt out
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_ke
                 for (int k = 0; k < nch; ++k) M = fmaxf(M, cm[k][hh]);
                 float num = 0.f, den = 0.f;
                 for (int k = 0; k < nch; ++k) {
-                    const float ac = expf(cm[k][hh] - M);
+                    const float ac = WA_CONTROL == 3 ? 1.f : expf(cm[k][hh] - M);
                     const float o = part[k][hh][tid];
                     num = fmaf(ac, o, num);
                     den = fmaf(ac, cl[k][hh], den);
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_ke
                     a.m[pi + tid] = cm[tid][hh];
                     a.l[pi + tid] = cl[tid][hh];
                 }
-                const uint32_t bits = f32_to_bf16_rne(num / den);
+                const uint32_t bits = merge_round(num / den);
                 a.out[(int64_t)r * a.o_srow + (int64_t)h * a.o_shead + tid] = (uint16_t)bits;
                 if (bf16_nonfinite((uint16_t)bits)) bad[hh] = 1;
             }

@@ -88,6 +88,18 @@ __device__ __forceinline__ int sigma(int i) {
     return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
+// Key range [lo, last] of prompt row `row` (a valid row): the window anchored on the row's
+// own position, the last key hi[row] clamped into [p0 + row, p0 + n - 1] or the position.
+__device__ __forceinline__ void prompt_span(const PromptArgs& a, int row, int& lo, int& last) {
+    const int p = a.p0 + row;
+    lo = a.window > 0 ? max(0, p - a.window + 1 - (WA_CONTROL == 2)) : 0;
+    last = p;
+    if (a.hi && WA_CONTROL != 5) {
+        const int hv = a.hi[row];
+        last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
+    }
+}
+
 // Both lane halves of a pair combined, on every lane, without an LDS round trip: the
 // half-swap (v_permlane32_swap) leaves lanes l and l ^ 32 holding each other's value in one of
 // its two results, and max / sum of the two results is the pair's (the same order of operands
@@ -216,15 +228,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 
     const int big = 0x7FFFFFFF;
     int lo = big, last = -1;                // empty range for padding pairs
-    if (valid) {
-        const int p = a.p0 + row;
-        lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-        last = p;
-        if (a.hi) {
-            const int hv = a.hi[row];
-            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
-        }
-    }
+    if (valid) prompt_span(a, row, lo, last);
     if constexpr (D == 256) load_q();
     // key range of this wave, the range all its valid pairs see, and the workgroup range
     const int w_kmin = wave_min_i(lo);
@@ -505,7 +509,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             for (int u = 0; u < 4; ++u) {
                 const float p0 = sacc[mb][r0 + 2 * u], p1 = sacc[mb][r0 + 2 * u + 1];
                 phi.w[u] = cvt_pk_bf16(p0, p1);
-                if (NP >= 2) {
+                if (NP == 2 && WA_CONTROL == 6) pmid.w[u] = 0u;
+                else if (NP >= 2) {
                     const float e0 = p0 - lo_bf16(phi.w[u]), e1 = p1 - hi_bf16(phi.w[u]);
                     pmid.w[u] = cvt_pk_bf16(e0, e1);
                     if (NP == 3) plo.w[u] = cvt_pk_bf16(e0 - lo_bf16(pmid.w[u]), e1 - hi_bf16(pmid.w[u]));
@@ -674,13 +679,8 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         const int64_t pr = first + i;
         if (pr >= npairs) break;
         const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
-        const int p = a.p0 + row;
-        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-        int last = p;
-        if (a.hi) {
-            const int hv = a.hi[row];
-            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
-        }
+        int lo, last;
+        prompt_span(a, row, lo, last);
         int nc = last / kPromptChunk - lo / kPromptChunk + 1;
         nc = nc > a.Cp ? a.Cp : nc;
         const int64_t pi = pr * a.Cp;     // (row * hq + head) * Cp
@@ -771,13 +771,8 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
     for (int f = 0; f < nf; ++f) {
         const int64_t pr = first + flagged[f];
         const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
-        const int p = a.p0 + row;
-        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-        int last = p;
-        if (a.hi) {
-            const int hv = a.hi[row];
-            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
-        }
+        int lo, last;
+        prompt_span(a, row, lo, last);
         uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
         const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
         rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
@@ -828,13 +823,8 @@ __global__ __launch_bounds__(D) void prompt_check_kernel(PromptArgs a) {
         const int64_t pr = first + flagged[i];
         const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
         uint16_t* orow = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead;
-        const int p = a.p0 + row;
-        const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-        int last = p;
-        if (a.hi) {
-            int hv = a.hi[row];
-            last = hv < p ? p : (hv > a.p0 + a.n - 1 ? a.p0 + a.n - 1 : hv);
-        }
+        int lo, last;
+        prompt_span(a, row, lo, last);
         const int64_t kv = (int64_t)(head / (a.hq / a.hkv)) * a.kv_shead;
         rerun_f64<D>(a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead, a.k + kv, a.v + kv,
                      a.kv_sslot, a.ring, lo, last, a.scale, orow);

@@ -4,6 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Planted mistakes for the GPU control tests, compiled only into separate control builds
+// (-DWA_CONTROL=k; the library itself is built with 0). After the planted controls of
+// TensorFold pull request #1123 ("Receipt", kernel-contract bullet):
+//   1 decode window one key early        2 prompt window one key early
+//   3 decode merge without exp(m_c - M)  4 decode merge rounding toward zero
+//   5 prompt rows ignoring hi             6 prompt P as one bf16 under p32
+#ifndef WA_CONTROL
+#define WA_CONTROL 0
+#endif
+
 namespace wa {
 
 constexpr int kChunk = 256;      // decode chunk: keys at absolute positions [256c, 256c + 255]
