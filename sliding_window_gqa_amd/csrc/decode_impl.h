@@ -147,7 +147,7 @@ __device__ __forceinline__ float unit_sum(const float (&v)[16], int dl) {
 }
 
 template <int D, int GMAX, bool WHOLE>
-__global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : 3) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3) void decode_kernel(DecodeArgs a) {
     constexpr int LPK = D / 8;               // lanes per key: 8 dims a lane
     constexpr int NRUN = kThreads / LPK;     // runs of consecutive keys per chunk
     constexpr int RUNLEN = kChunk / NRUN;    // keys per run
