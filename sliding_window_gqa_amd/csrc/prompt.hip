@@ -1,6 +1,8 @@
 // Launcher of the prompt form (wa_prompt, wa_prompt_sparse): grid shape, dispatch order and
 // the kernel variant for the head dim and the number of bf16 parts of P. The kernels and
-// their design are in prompt_impl.h; prompt_inst.hip instantiates them.
+// their design are in prompt_impl.h (128 pairs a workgroup: prompts at d = 128 and sparse
+// prompts) and prompt_quarter.h (dense prompts at d = 256); prompt_inst.hip instantiates
+// them.
 #include <atomic>
 
 #include "wa_common.h"
@@ -13,6 +15,9 @@ hipError_t launch_prompt_main_128_3(const PromptArgs&, int, unsigned, hipStream_
 hipError_t launch_prompt_main_256_1(const PromptArgs&, int, unsigned, hipStream_t);
 hipError_t launch_prompt_main_256_2(const PromptArgs&, int, unsigned, hipStream_t);
 hipError_t launch_prompt_main_256_3(const PromptArgs&, int, unsigned, hipStream_t);
+hipError_t launch_prompt_quarter_1(const PromptArgs&, hipStream_t);
+hipError_t launch_prompt_quarter_2(const PromptArgs&, hipStream_t);
+hipError_t launch_prompt_quarter_3(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_128(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_256(const PromptArgs&, hipStream_t);
 
@@ -35,6 +40,15 @@ int cu_count() {
 
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
     const int D = a.d;
+    if (D == 256 && !a.bm) {
+        // dense prompts at d = 256: every row finished inside one workgroup of the
+        // quarter-tile kernel (windowed or not), non-finite re-runs included
+        PromptArgs b = a;
+        b.nchunk = 1;
+        return a.p_parts == 3 ? launch_prompt_quarter_3(b, s)
+             : a.p_parts == 2 ? launch_prompt_quarter_2(b, s)
+                              : launch_prompt_quarter_1(b, s);
+    }
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPromptPairs - 1) / kPromptPairs);
     const unsigned grid = (unsigned)(nblk * a.hkv * a.nchunk);

@@ -88,11 +88,17 @@ __device__ __forceinline__ int sigma(int i) {
     return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
+// First key of prompt row `row`: the window anchored on the row's own position (non-
+// decreasing in the row).
+__device__ __forceinline__ int prompt_lo(const PromptArgs& a, int row) {
+    return a.window > 0 ? max(0, a.p0 + row - a.window + 1 - (WA_CONTROL == 2)) : 0;
+}
+
 // Key range [lo, last] of prompt row `row` (a valid row): the window anchored on the row's
 // own position, the last key hi[row] clamped into [p0 + row, p0 + n - 1] or the position.
 __device__ __forceinline__ void prompt_span(const PromptArgs& a, int row, int& lo, int& last) {
     const int p = a.p0 + row;
-    lo = a.window > 0 ? max(0, p - a.window + 1 - (WA_CONTROL == 2)) : 0;
+    lo = prompt_lo(a, row);
     last = p;
     if (a.hi && WA_CONTROL != 5) {
         const int hv = a.hi[row];

@@ -1,8 +1,9 @@
 // One instantiation of the prompt kernel (prompt_impl.h): head dim WA_INST_D with P in
-// WA_INST_NP bf16 parts; with WA_INST_POST also the merge and check kernels at that head dim.
+// WA_INST_NP bf16 parts, and at head dim 256 the quarter-tile kernel of dense prompts
+// (prompt_quarter.h); with WA_INST_POST also the merge and check kernels at that head dim.
 // The build compiles this file once per variant the launcher in prompt.hip calls, so that
 // they compile in parallel.
-#include "prompt_impl.h"
+#include "prompt_quarter.h"
 
 #if !defined(WA_INST_D) || !defined(WA_INST_NP) || !defined(WA_INST_POST)
 #error "prompt_inst.hip is compiled with -DWA_INST_D=.. -DWA_INST_NP=.. -DWA_INST_POST=0|1"
@@ -18,6 +19,11 @@ namespace wa {
 hipError_t WA_MAIN(WA_INST_D, WA_INST_NP)(const PromptArgs& b, int nblk, unsigned grid, hipStream_t s) {
     return launch_main<WA_INST_D, WA_INST_NP>(b, nblk, grid, s);
 }
+
+#if WA_INST_D == 256
+#define WA_QUARTER(np) WA_CAT2(launch_prompt_quarter_, np)
+hipError_t WA_QUARTER(WA_INST_NP)(const PromptArgs& b, hipStream_t s) { return launch_quarter<WA_INST_NP>(b, s); }
+#endif
 
 #if WA_INST_POST
 hipError_t WA_POST(WA_INST_D)(const PromptArgs& a, hipStream_t s) { return launch_post<WA_INST_D>(a, s); }
