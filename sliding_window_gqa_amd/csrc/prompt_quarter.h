@@ -10,8 +10,8 @@
 // one per SIMD. All four waves hold the same 32 pairs; they share every 64-key K/V tile in
 // LDS and wave w takes the keys 16w .. 16w + 15 of each tile (its quarter), with a running
 // (m, l, O) of its own over its quarters. After the last tile the four states are merged in
-// LDS in wave order: M = max m_w, a_w = 2^(m_w - M), out = bf16(sum a_w O_w / sum a_w l_w),
-// both sums fma chains in w order. So every row is finished inside its workgroup: no fp32
+// LDS in wave order: M = max m_w, a_w = 2^(m_w - M), den = sum a_w l_w, out =
+// bf16(sum (a_w / den) O_w), the sums fma chains in w order. So every row is finished inside its workgroup: no fp32
 // partials leave the CU and no merge kernel follows; a (row, head) whose bf16 output is not
 // finite is re-run in float64 by the same workgroup (rerun_f64.h), so no check kernel
 // follows either. A row's bits depend only on its key
@@ -406,29 +406,29 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         step(t, Ks0, Vs0, Ks1, Vs1, t + 1 <= t1);
         if (t + 1 <= t1) step(t + 1, Ks1, Vs1, Ks0, Vs0, t + 2 <= t1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();                       // every wave done with the stage arrays
-
-    // merge of the four quarters' states: wave w stores its O (pair-major, the 16-byte chunk
-    // k of pair p at k ^ (p & 15)) into array w, and (m, l) into red_*
+    // merge of the four quarters' states. A wave's own rows of the four stage arrays (rows
+    // 16w .. 16w + 15 of every tile, 8 KiB in each) are touched by no other wave and hold
+    // exactly its O: once its own loads have landed it stores O there without waiting for
+    // the other waves, dims 64j .. 64j + 63 into array j (pair-major, 256 bytes a pair, the
+    // 16-byte chunk c of pair p at c ^ (p & 15)), and (m, l) into red_*.
     const float l_tot = pair_sum(l_run);
-    const char* const arrs[kWaves] = {Ks0, Vs0, Ks1, Vs1};
-    {
-        char* const mine = wave == 0 ? Ks0 : wave == 1 ? Vs0 : wave == 2 ? Ks1 : Vs1;
-        float* ob = reinterpret_cast<float*>(mine) + col * D;
+    char* const arrs[kWaves] = {Ks0, Vs0, Ks1, Vs1};
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int k = 8 * db + 2 * q4 + h;          // dims 4k .. 4k + 3
-                *reinterpret_cast<float4*>(ob + 4 * (k ^ (col & 15))) =
-                    make_float4(oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]);
-            }
-        if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
-    }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * h;        // dims d0 .. d0 + 3
+            const int c = (d0 & 63) >> 2;                   // chunk within the 64-dim block
+            float* ob = reinterpret_cast<float*>(arrs[d0 >> 6] + 16 * RB * wave) + col * 64;
+            *reinterpret_cast<float4*>(ob + 4 * (c ^ (col & 15))) =
+                make_float4(oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]);
+        }
+    if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
     lds_barrier();
-    // wave w produces dims 64w + 32h + 0..31 of pair col; a (row, head) with a non-finite value
-    // is flagged before any of its values is stored, and re-run below instead
+    // wave w produces dims 64w + 32h + 0..31 of pair col from array w; a (row, head) with a
+    // non-finite value is flagged before any of its values is stored, and re-run below instead
+    const char* const mine = wave == 0 ? Ks0 : wave == 1 ? Vs0 : wave == 2 ? Ks1 : Vs1;
     uint2 res[8];
     if (valid) {
         float M = -INFINITY;
@@ -441,25 +441,32 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
             ac[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             den = fmaf(ac[w], red_l[w][col], den);
         }
-        bool nonfinite = false;
+        // out = sum_w (a_w / den) O_w: one division a lane instead of one per value (den = 0,
+        // a row without keys, gives NaN and a float64 re-run, as 0 / 0 would)
+        const float rden = 1.f / den;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) ac[w] *= rden;
+        uint32_t expo = 0;                 // OR of the exponent fields: all ones = not finite
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int k = 16 * wave + 8 * h + i;
+            const int c = 8 * h + i;                         // dims 64 wave + 4c .. + 3
             float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(arrs[w]) + col * D + 4 * (k ^ (col & 15)));
+                const float4 o = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(mine + 16 * RB * w) + col * 64 + 4 * (c ^ (col & 15)));
                 num.x = fmaf(ac[w], o.x, num.x);
                 num.y = fmaf(ac[w], o.y, num.y);
                 num.z = fmaf(ac[w], o.z, num.z);
                 num.w = fmaf(ac[w], o.w, num.w);
             }
-            res[i].x = pack_bf16x2(num.x / den, num.y / den);
-            res[i].y = pack_bf16x2(num.z / den, num.w / den);
-            nonfinite |= bf16_nonfinite(res[i].x & 0xFFFFu) || bf16_nonfinite(res[i].x >> 16) ||
-                         bf16_nonfinite(res[i].y & 0xFFFFu) || bf16_nonfinite(res[i].y >> 16);
+            res[i].x = cvt_pk_bf16(num.x, num.y);
+            res[i].y = cvt_pk_bf16(num.z, num.w);
+            const uint32_t e0 = res[i].x & 0x7F807F80u, e1 = res[i].y & 0x7F807F80u;
+            expo |= ((e0 & 0x7F80u) == 0x7F80u) | ((e0 >> 16) == 0x7F80u) |
+                    ((e1 & 0x7F80u) == 0x7F80u) | ((e1 >> 16) == 0x7F80u);
         }
-        if (nonfinite) bad[col] = 1;
+        if (expo) bad[col] = 1;
     }
     lds_barrier();
     if (valid && !bad[col]) {
