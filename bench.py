@@ -525,8 +525,9 @@ def main():
     rl_decode_alu = roofline("alu", dec_tfs, DECODE_VALU_PEAK_TFS, "TFLOP/s", dec_traffic,
                              "decode_kernel<256,2,chunks> + merge_kernel (fp32 q.k dot2 + p.v fma)")
     rl_prompt = roofline("mfma", pre_tfs, MFMA_BF16_PEAK_TFS, "TFLOP/s",
-                         traffic_bytes("prompt12b", ["prompt_kernel", "prompt_merge_kernel"]),
-                         "prompt_kernel<256,p32> + prompt_merge_kernel, one call (12B prompt chunk)")
+                         traffic_bytes("prompt12b", ["prompt_quarter_kernel"]),
+                         "prompt_quarter_kernel<p32>, one call (12B prompt chunk: the whole call "
+                         "is this one kernel)")
     res["roofline"] = rl_prompt if pms >= dms else rl_decode
     res["roofline_decode"] = rl_decode
     res["roofline_decode_alu"] = rl_decode_alu
@@ -573,8 +574,9 @@ def main():
                           "flop_accounting": "(2 + 2*1) * d per visible (row, head, key), bf16 P"}
     res["roofline_prefill_31b"] = roofline(
         "mfma", ctf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
-        traffic_bytes("prompt31b", ["prompt_kernel", "prompt_merge_kernel"]),
-        "prompt_kernel<256,bf16P> + prompt_merge_kernel, one call (31B prompt chunk)")
+        traffic_bytes("prompt31b", ["prompt_quarter_kernel"]),
+        "prompt_quarter_kernel<bf16P>, one call (31B prompt chunk: the whole call is this one "
+        "kernel)")
 
     if not args.no_long:
         lcase = cases["C5"]
