@@ -3,8 +3,6 @@
 // their design are in prompt_impl.h (128 pairs a workgroup: prompts at d = 128 and sparse
 // prompts) and prompt_quarter.h (dense prompts at d = 256); prompt_inst.hip instantiates
 // them.
-#include <atomic>
-
 #include "wa_common.h"
 
 namespace wa {
@@ -21,23 +19,6 @@ hipError_t launch_prompt_quarter_3(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_128(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_256(const PromptArgs&, hipStream_t);
 
-namespace {
-
-// Compute units of the current device, queried once per device (the query costs
-// microseconds of host time, which would land between a caller's events and the launch).
-int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cache[dev].store(c, std::memory_order_relaxed);
-    return c;
-}
-
-}  // namespace
-
 hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
     const int D = a.d;
     if (D == 256 && !a.bm) {
@@ -52,11 +33,7 @@ hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPromptPairs - 1) / kPromptPairs);
     const unsigned grid = (unsigned)(nblk * a.hkv * a.nchunk);
-    // chunk-major dispatch (dense prompts at d = 256, one workgroup a CU) when all but the
-    // last chunk slot of every group fit in one round; measured no faster for sparse prompts,
-    // whose empty slots are not the last ones
-    PromptArgs b = a;
-    b.chunk_major = D == 256 && !a.bm && a.nchunk > 1 && (int64_t)nblk * a.hkv * (a.nchunk - 1) <= cu_count();
+    const PromptArgs& b = a;
     hipError_t e;
     if (D == 256) {
         e = a.p_parts == 3 ? launch_prompt_main_256_3(b, nblk, grid, s)

@@ -26,10 +26,9 @@
 //     by buffer loads with a per-tile descriptor on interior tiles; K fragments are 16-byte
 //     LDS reads, V^T fragments come from the transposing LDS read (ds_read_b64_tr_b16); the
 //     tiles are double buffered, the next tile's loads are in flight while the current tile
-//     computes, and there is one barrier per tile; dense prompts at d = 256 and unsplit dense
-//     prompts at d = 128 walk the tiles software-pipelined (tile t + 1's score MFMAs are
-//     issued before tile t's softmax, K is fetched two tiles ahead and V one), with each
-//     tile's arithmetic unchanged;
+//     computes, and there is one barrier per tile; unsplit dense prompts at d = 128 walk the
+//     tiles software-pipelined (tile t + 1's score MFMAs are issued before tile t's softmax,
+//     K is fetched two tiles ahead and V one), with each tile's arithmetic unchanged;
 //   * the K rows of a tile are fed to the first MFMA in a permuted order so that the S^T
 //     accumulator registers of a lane are, eight at a time, exactly the B operand (P^T) the
 //     P.V MFMA needs for eight consecutive keys: no shuffles between the two products;
@@ -38,11 +37,12 @@
 //     exceeds it by more than 2^8 in probability), so the O rescale runs on few tiles;
 //   * the workgroup index is remapped so that each XCD (8 on MI355X, workgroups dealt out
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
-//     a key head's K/V stream in that XCD's L2 (chunk-major inside the range when the
-//     launcher asks for it);
+//     a key head's K/V stream in that XCD's L2;
 //   * at d = 256 (one wave a SIMD) the MFMA accumulators stay in VGPRs (the library is built
 //     with -amdgpu-mfma-vgpr-form), the V^T fragments of the next 16-key step are read while
 //     the current step's MFMAs run, and the Q loads stay in flight across the set-up.
+// This kernel serves prompts at d = 128 and block-sparse prompts at d = 256; dense prompts at
+// d = 256 take the quarter-tile kernel (prompt_quarter.h).
 //
 // This header holds the kernels; prompt_inst.hip instantiates them once per (head dim, parts
 // of P), so that they compile in parallel, and prompt.hip holds the launcher.
@@ -173,31 +173,11 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
 
     // XCD-aware remap of the linear workgroup index (the hardware deals ids out to the 8 XCDs
     // in turn): XCD x takes a contiguous share of the logical ids (key head, block of pairs,
-    // chunk), so one head's K/V stream stays in its L2. With chunk_major the XCD walks its
-    // share chunk-major (every group's first chunk, then every group's second, ...): the
-    // last chunk slots, empty for most groups, are then dispatched last instead of holding
-    // CUs while working workgroups wait (the launcher sets it for dense d = 256 prompts whose
-    // other slots fit in one round of workgroups).
+    // chunk), so one head's K/V stream stays in its L2.
     const int total = gridDim.x;
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int per = total >> 3, extra = total & 7;
-    const int share0 = xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per;
-    int logical = share0 + idx;
-    if (D == 256 && a.chunk_major) {
-        const int share1 = share0 + (xcd < extra ? per + 1 : per);
-        const int nc = a.nchunk;
-        int rem = idx;
-        for (int c = 0; c < nc; ++c) {
-            // ids l of the share with l % nc == c: the first one, and how many
-            const int l0 = share0 + (c - share0 % nc + nc) % nc;
-            const int cnt = l0 < share1 ? (share1 - 1 - l0) / nc + 1 : 0;
-            if (rem < cnt) { logical = l0 + rem * nc; break; }
-            rem -= cnt;
-        }
-        // the same for every lane: keep it in a scalar register, so that everything derived
-        // from it (and the branches on it) stays scalar
-        logical = __builtin_amdgcn_readfirstlane(logical);
-    }
+    const int logical = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + idx;
     const int cidx = logical % a.nchunk;    // key chunk of the workgroup's range (split mode)
     const int gb = logical / a.nchunk;
     const int g = gb / nblk;                // key head
@@ -582,11 +562,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         __syncthreads();
     };
 
-    // dense prompts at d = 256 (split or not) and unsplit dense prompts at d = 128 (the long
-    // ones) walk their tiles software-pipelined
+    // unsplit dense prompts at d = 128 (the long ones) walk their tiles software-pipelined
+    // (this kernel sees d = 256 only for sparse prompts: dense ones take prompt_quarter.h)
     bool piped = false;
     if constexpr (D == 128) piped = !split && !sparse;
-    if constexpr (D == 256) piped = !sparse;
     if (piped) {
         // A software-pipelined walk. While tile t's
         // softmax runs on the VALU, tile t + 1's scores are already on the matrix cores; K is

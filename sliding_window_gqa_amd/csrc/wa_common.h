@@ -68,7 +68,6 @@ struct PromptArgs {
     // key-chunk split (windowed prompts): nchunk = key chunks per workgroup grid slot
     // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials
     int32_t nchunk, Cp;
-    int32_t chunk_major;          // set by the launcher: dispatch each XCD's share chunk-major
     float* pm; float* pl; float* po;
     // block-sparse prompts: row i sees only the keys of its range whose 64-key block b has
     // bit b % 32 of word b / 32 set in bm[i * bm_srow ..] (words past bm_words: not
