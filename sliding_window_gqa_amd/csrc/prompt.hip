@@ -1,8 +1,8 @@
 // Launcher of the prompt form (wa_prompt, wa_prompt_sparse): grid shape, dispatch order and
 // the kernel variant for the head dim and the number of bf16 parts of P. The kernels and
-// their design are in prompt_impl.h (128 pairs a workgroup: prompts at d = 128 and sparse
-// prompts) and prompt_quarter.h (dense prompts at d = 256); prompt_inst.hip instantiates
-// them.
+// their design are in prompt_impl.h (128 pairs a workgroup: prompts at d = 128),
+// prompt_quarter.h (dense prompts at d = 256) and prompt_sparse.h (block-sparse prompts at
+// d = 256); prompt_inst.hip instantiates them.
 #include "wa_common.h"
 
 namespace wa {
@@ -16,6 +16,9 @@ hipError_t launch_prompt_main_256_3(const PromptArgs&, int, unsigned, hipStream_
 hipError_t launch_prompt_quarter_1(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_quarter_2(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_quarter_3(const PromptArgs&, hipStream_t);
+hipError_t launch_prompt_rows_1(const PromptArgs&, hipStream_t);
+hipError_t launch_prompt_rows_2(const PromptArgs&, hipStream_t);
+hipError_t launch_prompt_rows_3(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_128(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_post_256(const PromptArgs&, hipStream_t);
 
@@ -29,6 +32,18 @@ hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
         return a.p_parts == 3 ? launch_prompt_quarter_3(b, s)
              : a.p_parts == 2 ? launch_prompt_quarter_2(b, s)
                               : launch_prompt_quarter_1(b, s);
+    }
+    if (D == 256) {
+        // block-sparse prompts at d = 256: row groups over 4096-key segments at absolute
+        // positions, then the ordered merge of the segments' partials
+        PromptArgs b = a;
+        b.chunk_keys = kSparseSeg;
+        b.nchunk = b.Cp = sparse_segments(a.window, a.p0, a.n);
+        const hipError_t e = a.p_parts == 3 ? launch_prompt_rows_3(b, s)
+                           : a.p_parts == 2 ? launch_prompt_rows_2(b, s)
+                                            : launch_prompt_rows_1(b, s);
+        if (e != hipSuccess) return e;
+        return launch_prompt_post_256(b, s);
     }
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPromptPairs - 1) / kPromptPairs);

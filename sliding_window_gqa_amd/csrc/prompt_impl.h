@@ -666,20 +666,26 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
         const int row = (int)(pr / a.hq), head = (int)(pr % a.hq);
         int lo, last;
         prompt_span(a, row, lo, last);
-        int nc = last / kPromptChunk - lo / kPromptChunk + 1;
+        const int CK = a.chunk_keys;
+        int nc = last / CK - lo / CK + 1;
         nc = nc > a.Cp ? a.Cp : nc;
         const int64_t pi = pr * a.Cp;     // (row * hq + head) * Cp
         // Does chunk c (of the row's range) hold one of the row's keys? Every chunk of a
         // dense range does; a sparse row's chunk only through a selected block that meets
         // [lo, last] -- the rule the prompt kernel writes partials by.
         const uint32_t* brow = a.bm ? a.bm + (int64_t)row * a.bm_srow : nullptr;
+        // The blocks that meet [lo, last] are lo / 64 .. last / 64; the chunk's share of them,
+        // b0 .. b1, is tested a mask word at a time.
         auto present = [&](int c) {
             if (c >= nc) return false;
             if (!brow) return true;
-            const int c0 = (lo / kPromptChunk + c) * (kPromptChunk / kSparseBlock);
-            for (int b = c0; b < c0 + kPromptChunk / kSparseBlock; ++b)
-                if (block_selected(brow, a.bm_words, b) && kSparseBlock * b <= last && kSparseBlock * b + kSparseBlock - 1 >= lo)
-                    return true;
+            const int nb = CK / kSparseBlock;
+            const int c0 = (lo / CK + c) * nb;
+            const int b0 = max(c0, lo / kSparseBlock), b1 = min(c0 + nb - 1, last / kSparseBlock);
+            for (int w = b0 >> 5; w <= (b1 >> 5) && w < a.bm_words; ++w) {
+                const int s = max(b0 - 32 * w, 0), e = min(b1 - 32 * w, 31);
+                if (s <= e && (brow[w] & (0xFFFFFFFFu >> (31 - e)) & (0xFFFFFFFFu << s))) return true;
+            }
             return false;
         };
         const float* op = a.po + pi * D + DL * lane;

@@ -1,9 +1,10 @@
 // One instantiation of the prompt kernel (prompt_impl.h): head dim WA_INST_D with P in
 // WA_INST_NP bf16 parts, and at head dim 256 the quarter-tile kernel of dense prompts
-// (prompt_quarter.h); with WA_INST_POST also the merge and check kernels at that head dim.
+// (prompt_quarter.h) and the row-group kernel of block-sparse prompts (prompt_sparse.h); with
+// WA_INST_POST also the merge and check kernels at that head dim.
 // The build compiles this file once per variant the launcher in prompt.hip calls, so that
 // they compile in parallel.
-#include "prompt_quarter.h"
+#include "prompt_sparse.h"
 
 #if !defined(WA_INST_D) || !defined(WA_INST_NP) || !defined(WA_INST_POST)
 #error "prompt_inst.hip is compiled with -DWA_INST_D=.. -DWA_INST_NP=.. -DWA_INST_POST=0|1"
@@ -22,7 +23,9 @@ hipError_t WA_MAIN(WA_INST_D, WA_INST_NP)(const PromptArgs& b, int nblk, unsigne
 
 #if WA_INST_D == 256
 #define WA_QUARTER(np) WA_CAT2(launch_prompt_quarter_, np)
+#define WA_ROWS(np) WA_CAT2(launch_prompt_rows_, np)
 hipError_t WA_QUARTER(WA_INST_NP)(const PromptArgs& b, hipStream_t s) { return launch_quarter<WA_INST_NP>(b, s); }
+hipError_t WA_ROWS(WA_INST_NP)(const PromptArgs& b, hipStream_t s) { return launch_rows<WA_INST_NP>(b, s); }
 #endif
 
 #if WA_INST_POST

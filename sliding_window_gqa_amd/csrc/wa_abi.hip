@@ -207,7 +207,7 @@ int wa_prompt(const wa_window_t* w,
     a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p_parts = 1 + w->p32;
     a.hi = hi;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
-    a.nchunk = 1; a.Cp = 0; a.pm = a.pl = a.po = nullptr;
+    a.nchunk = 1; a.Cp = 0; a.chunk_keys = wa::kPromptChunk; a.pm = a.pl = a.po = nullptr;
     if (w->window > 0) {
         const size_t need = wa_prompt_workspace(w, n, hq, d);
         if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return WA_EWORKSPACE;
@@ -268,6 +268,7 @@ int wa_prompt_sparse(const wa_window_t* w,
     a.bm = blocks; a.bm_srow = blocks_srow; a.bm_words = blocks_words;
     a.nchunk = wa::sparse_chunks(w->window, p0, n);
     a.Cp = a.nchunk;
+    a.chunk_keys = wa::kPromptChunk;
     const size_t cells = (size_t)n * hq * a.Cp;
     a.pm = static_cast<float*>(ws);
     a.pl = a.pm + cells;

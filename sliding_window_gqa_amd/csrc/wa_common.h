@@ -66,8 +66,9 @@ struct PromptArgs {
     const int32_t* hi;
     uint16_t* out; int64_t o_srow, o_shead;
     // key-chunk split (windowed prompts): nchunk = key chunks per workgroup grid slot
-    // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials
-    int32_t nchunk, Cp;
+    // (1 = no split), Cp = chunk capacity per (row, head) of the fp32 partials, chunk_keys =
+    // keys per chunk at absolute positions (set by the launcher for the kernel it picks)
+    int32_t nchunk, Cp, chunk_keys;
     float* pm; float* pl; float* po;
     // block-sparse prompts: row i sees only the keys of its range whose 64-key block b has
     // bit b % 32 of word b / 32 set in bm[i * bm_srow ..] (words past bm_words: not
@@ -86,6 +87,12 @@ __device__ __forceinline__ bool block_selected(const uint32_t* row_mask, int wor
 // prompt split: keys [384c, 384c + 383], absolute (six 64-key tiles: a 1024-key window over a
 // 512-row chunk then fills the GPU in one round of workgroups)
 constexpr int kPromptChunk = 384;
+// block-sparse prompts at d = 256: 4096-key segments at absolute positions (64 blocks, two mask
+// words), one workgroup a (row group, key head, segment)
+constexpr int kSparseSeg = 4096;
+inline int sparse_segments(int window, int p0, int n) {
+    return window > 0 ? (window - 1 + n) / kSparseSeg + 2 : (p0 + n - 1) / kSparseSeg + 1;
+}
 
 // (row, query head) pairs per workgroup of the prompt kernel (4 waves of 32)
 constexpr int kPromptPairs = 128;
