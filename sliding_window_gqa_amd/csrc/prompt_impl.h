@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     // loads of one tile of K (or V) into an LDS stage
     auto issue_half = [&](int tile, char* dst, const uint16_t* src) __attribute__((always_inline)) {
         const int base = tile * BN;
-        const int sbase = base % a.ring;
+        const int sbase = ring_slot(a, base);
         if (base >= kmin && base + BN - 1 <= kmax && sbase + BN <= a.ring) {
             const int64_t toff = (int64_t)sbase * a.kv_sslot;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + toff), (short)0, tile_extent, 0x00020000);

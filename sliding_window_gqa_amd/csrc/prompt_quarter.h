@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     auto prep = [&](int tile, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
         QLoad L;
         L.qb = tile * BN + 16 * wave;
-        L.sq = L.qb % a.ring;
+        L.sq = ring_slot(a, L.qb);
         L.kcap = kcap;
         L.kd = kdst + 16 * RB * wave;
         L.vd = vdst + 16 * RB * wave;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         // fast path (those loads then touch no memory), so that every quarter issues the same
         // loads at the same places and waits the same way
         const int nqb = (tile + 1) * BN + 16 * wave;
-        const int nsq = nqb % a.ring;
+        const int nsq = ring_slot(a, nqb);
         const int nrec = nxt ? quarter_extent : 0;
         const int64_t nso = (int64_t)nsq * a.kv_sslot;
         const __amdgpu_buffer_rsrc_t nrk = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + nso), (short)0, nrec, 0x00020000);

@@ -12,25 +12,30 @@
 // columns share one row's selection and the walk has no union of other rows' blocks to
 // carry -- and one 4096-key segment at absolute positions (64 blocks, two mask words). Its
 // four waves, one a SIMD, all hold the same columns; wave w takes keys 16w .. 16w + 15 of
-// every selected block (its quarter) with a running (m, l, O) of its own, loading only its
-// own 16 rows of K and V (double-buffered, no barrier in the walk).
-//   * S^T of a quarter (16 keys x 16 columns) is one v_mfma_f32_16x16x32_bf16 product over
-//     eight 32-dim steps (two chains, even and odd steps, added at the end); its
-//     accumulator layout (lane l: keys 4 (l / 16) + i of column l % 16) is exactly the
-//     B operand of v_mfma_f32_16x16x16bf16_1k, so P goes to P.V without a shuffle;
+// every selected block (its quarter) with a running (m, l, O) of its own, and walks the
+// selected blocks two at a time (a and b; b absent at an odd end):
+//   * K goes from memory straight into registers in the score product's operand layout
+//     (lane l: key l % 16 of the quarter, dims 32 ks + 8 (l / 16) + 0..7), the next two
+//     quarters' loads issued as soon as the score products have read this step's;
+//   * S^T of a quarter (16 keys x 16 columns) is one chain of eight v_mfma_f32_16x16x32_bf16
+//     products; lane l then holds keys 4 (l / 16) + i of column l % 16 for both blocks, and
+//     those eight values, a's four then b's four, are exactly the B operand (32 keys) of a
+//     v_mfma_f32_16x16x32_bf16 P.V product whose A operand puts the same keys in the same
+//     order: the transposing LDS reads (ds_read_b64_tr_b16) of the two blocks' V, side by side;
+//   * V goes into LDS (the transposing reads need it there) by buffer_load ... lds into two
+//     stages of two blocks each, each wave loading only its own 16 rows: no barrier in the walk;
 //   * the column's row maximum and sum span the four lanes l % 16 + 16k: one
 //     v_permlane16_swap and one v_permlane32_swap step;
-//   * O^T += V^T P^T: sixteen 16-dim blocks, NP products each, V^T by the transposing LDS
-//     read (ds_read_b64_tr_b16); O^T holds 64 registers a lane;
-//   * the next quarter's loads go out one after each score step (K) and one after every
-//     other 16-dim block of P.V (V), as in prompt_quarter.h;
 //   * after the walk the four states are merged in LDS in wave order (M = max m_w,
 //     a_w = 2^(m_w - M), l = sum a_w l_w, o = sum a_w O_w) and written as the segment's fp32
 //     partial (m in log2 units), which prompt_merge_kernel combines over the segments in
 //     order, with the float64 re-run of non-finite rows. A segment holding none of a row's
 //     selected keys writes no partial for it (the merge applies the same rule).
 // A row's bits depend only on its range, its selection, the absolute block and segment grid
-// and the quarter split, never on the other rows of its call or on how the prompt is cut.
+// and the quarter split and pairing of the walk, never on the other rows of its call or on how
+// the prompt is cut: the pairing is that of the row's own selection when the workgroup holds
+// one row; with several rows (few query heads a key head) a block another row selected can
+// change the pairing, within the tolerance of the fp32 sums.
 #pragma once
 
 #include "prompt_quarter.h"
@@ -41,7 +46,25 @@ namespace {
 
 constexpr int kRowCols = 16;           // (row, head) columns per workgroup
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// LDS loads issued as inline assembly (they write LDS only, no register): the compiler does not
+// track them, so each wait on them is written out (lds_dma_wait_vm16, s_waitcnt before the
+// results are read). M0 holds the wave's LDS destination; lane i's 16 bytes land at M0 + 16 i.
+// Volatile statements keep their order among themselves; the waits below also order every
+// memory access around them, so an LDS read and the load that refills its stage stay on either
+// side of a wait.
+__device__ __forceinline__ void lds_dma_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(m0), "s"(rsrc));
+}
+__device__ __forceinline__ void lds_dma_global16(const void* src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0));
+}
+// all but the last 16 vector-memory loads have landed; all have
+__device__ __forceinline__ void lds_dma_wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void lds_dma_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// every LDS read issued so far has returned
+__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ int ctz64(uint64_t x) { return __builtin_ctzll(x); }
 
@@ -50,19 +73,18 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
     constexpr int D = 256;
     constexpr int KS = D / 32;             // 32-dim steps of S^T
     constexpr int DB = D / 16;             // 16-dim blocks of O^T
-    constexpr int RB = 2 * D;              // bytes per K/V row in LDS
+    constexpr int RB = 2 * D;              // bytes per V row in LDS
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     constexpr int RPK = 1024 / RB;         // rows per 1 KiB wave load
     constexpr int TILE_B = BN * RB;        // bytes of one K (or V) tile
     constexpr int QL = 16 * RB / 1024;     // wave loads per quarter (each of K and V)
     constexpr int SEGB = kSparseSeg / kSparseBlock;   // blocks a segment (one or two mask words)
     static_assert(SEGB == 32 || SEGB == 64, "a segment is one or two whole mask words");
-    static_assert(QL == KS && 2 * QL == DB, "one K load per score step, one V load per two O blocks");
-    // two stages of K and V; wave w owns rows 16w .. 16w + 15 of each (8 KiB an array)
-    __shared__ __attribute__((aligned(1024))) char Ks0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Vs0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Ks1[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Vs1[TILE_B];
+    static_assert(2 * QL == DB, "one V load after each 16-dim block of P.V (two quarters a step)");
+    // K and V of the two blocks of a step, one stage each: block a in Ks[0] / Vs[0], b in
+    // Ks[1] / Vs[1]; wave w owns rows 16w .. 16w + 15 of each (8 KiB an array)
+    __shared__ __attribute__((aligned(1024))) char Ks[2][TILE_B];
+    __shared__ __attribute__((aligned(1024))) char Vs[2][TILE_B];
     __shared__ float red_m[kWaves][kRowCols];
     __shared__ float red_l[kWaves][kRowCols];
 
@@ -135,7 +157,12 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
     const uint16_t* kg = a.k + (int64_t)g * a.kv_shead;
     const uint16_t* vg = a.v + (int64_t)g * a.kv_shead;
 
-    // quarter loads (own rows), as in prompt_quarter.h
+    // Loads of a quarter (own 16 rows of block `tile`, K or V, into `dst`): 16 bytes a lane
+    // straight into LDS (buffer_load ... lds / global_load_lds, issued by the lds_dma_* helpers
+    // so that the waits below are the only ones on them: the compiler would otherwise make every
+    // LDS read wait for all such loads in flight). A quarter with every key inside [kmin, kmax]
+    // and no ring wrap goes by buffer loads from a descriptor on its first slot (no records:
+    // zeros, for an absent block), an edge quarter key by key. Every quarter issues QL loads.
     const int ld_row = lane / CPR, ld_p = lane % CPR;
     uint32_t lane_off[QL];
 #pragma unroll
@@ -147,54 +174,69 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
     const int quarter_extent = (int)((uint32_t)(15 * a.kv_sslot) * 2u + 2u * D);
     auto is_fast = [&](int tile) __attribute__((always_inline)) {
         const int qb = tile * BN + 16 * wave;
-        return qb >= kmin && qb + 15 <= kmax && qb % a.ring + 16 <= a.ring;
+        return qb >= kmin && qb + 15 <= kmax && ring_slot(a, qb) + 16 <= a.ring;
     };
-    auto qdesc = [&](int tile, const uint16_t* src, bool use) __attribute__((always_inline)) {
-        const int qb = tile * BN + 16 * wave;
-        const int sq = qb % a.ring;
+    auto qdesc = [&](const uint16_t* src, int tile, bool use) __attribute__((always_inline)) {
+        const int sq = ring_slot(a, tile * BN + 16 * wave);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(src + (int64_t)sq * a.kv_sslot), (short)0,
-                                                 use && is_fast(tile) ? quarter_extent : 0, 0x00020000);
+                                                 use ? quarter_extent : 0, 0x00020000);
     };
-    // a whole quarter, key by key (clamped into [kmin, kmax], wrapped into the ring), K's first.
-    // A selected tile may hold quarters wholly below kmin or above kmax; the slot is counted
-    // from the quarter's first key clamped into [kmin, kmax], so that every clamped key lies
-    // 0 .. 15 keys after it (one wrap at most in a ring of at least 16 slots).
-    auto issue_edge = [&](int tile, char* kdst, char* vdst) __attribute__((always_inline)) {
+    auto lds_base = [&](const char* dst) __attribute__((always_inline)) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(uint32_t)(uintptr_t)(lds_void_ptr)(dst + 16 * RB * wave));
+    };
+    // a quarter key by key: key qb + r clamped into [kmin, kmax] and wrapped into the ring,
+    // counted from the quarter's first key clamped into that range (every clamped key lies
+    // 0 .. 15 keys after it: one wrap at most in a ring of at least 16 slots; a selected block
+    // may hold quarters wholly below kmin or above kmax)
+    auto issue_edge = [&](const uint16_t* src, int tile, const char* dst) __attribute__((always_inline)) {
         const int qb = tile * BN + 16 * wave;
         const int qbc = min(max(qb, kmin), kmax);
-        const int sqc = qbc % a.ring;
+        const int sqc = ring_slot(a, qbc);
+        int slot[QL];
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int i = 0; i < QL; ++i) slot[i] = sqc + (min(max(qb + RPK * i + ld_row, kmin), kmax) - qbc);
+        if (a.ring >= 16) {
 #pragma unroll
-            for (int i = 0; i < QL; ++i) {
-                const int r = RPK * i + ld_row;
-                const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
-                const int jc = min(max(qb + r, kmin), kmax);
-                int slot = sqc + (jc - qbc);
-                if (a.ring >= 16) slot = slot >= a.ring ? slot - a.ring : slot;
-                else slot = jc % a.ring;
-                const uint16_t* src = half ? vg : kg;
-                char* dst = (half ? vdst : kdst) + 16 * RB * wave + 1024 * i;
-                __builtin_amdgcn_global_load_lds(src + (int64_t)slot * a.kv_sslot + 8 * c,
-                                                 (lds_void_ptr)dst, 16, 0, 0);
-            }
+            for (int i = 0; i < QL; ++i) slot[i] = slot[i] >= a.ring ? slot[i] - a.ring : slot[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < QL; ++i) slot[i] = min(max(qb + RPK * i + ld_row, kmin), kmax) % a.ring;
+        }
+        const uint32_t m0 = lds_base(dst);
+#pragma unroll
+        for (int i = 0; i < QL; ++i) {
+            const int r = RPK * i + ld_row;
+            const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
+            lds_dma_global16(src + (int64_t)slot[i] * a.kv_sslot + 8 * c, m0 + 1024 * i);
+        }
     };
-    auto issue_fast = [&](int tile, char* kdst, char* vdst) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rk = qdesc(tile, kg, true), rv = qdesc(tile, vg, true);
+    // a whole quarter now (`use` false: zeros)
+    auto issue_quarter = [&](const uint16_t* src, int tile, bool use, const char* dst) __attribute__((always_inline)) {
+        if (use && !is_fast(tile)) {
+            issue_edge(src, tile, dst);
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = qdesc(src, tile, use);
+            const uint32_t m0 = lds_base(dst);
 #pragma unroll
-        for (int i = 0; i < QL; ++i) buffer_to_lds16(rk, kdst + 16 * RB * wave + 1024 * i, lane_off[i]);
-#pragma unroll
-        for (int i = 0; i < QL; ++i) buffer_to_lds16(rv, vdst + 16 * RB * wave + 1024 * i, lane_off[i]);
-    };
-    auto issue_whole = [&](int tile, char* kdst, char* vdst) __attribute__((always_inline)) {
-        if (is_fast(tile)) issue_fast(tile, kdst, vdst);
-        else issue_edge(tile, kdst, vdst);
+            for (int i = 0; i < QL; ++i) lds_dma_buffer16(rs, lane_off[i], m0 + 1024 * i);
+        }
     };
 
+    // the walk's first step: blocks a and b (b absent: zeros for its K and V, its scores masked)
     uint64_t rem = tiles;
-    int cur = tb0 + ctz64(rem);
-    rem &= rem - 1;
-    issue_whole(cur, Ks0, Vs0);
+    auto take = [&]() __attribute__((always_inline)) {
+        const int t = tb0 + ctz64(rem);
+        rem &= rem - 1;
+        return t;
+    };
+    int ta = take();
+    bool hb = rem != 0;
+    int tb = hb ? take() : ta;
+    issue_quarter(vg, ta, true, Vs[0]);
+    issue_quarter(vg, tb, hb, Vs[1]);
+    issue_quarter(kg, ta, true, Ks[0]);
+    issue_quarter(kg, tb, hb, Ks[1]);
 
     // Q^T operand of the score product: lane l holds column l % 16 at dims 32 ks + 8 (l / 16)
     // + 0..7 (a padding column takes a valid row's q; its scores are never used)
@@ -204,6 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 32 * ks);
     }
+    // every load so far has landed: from here on the walk's own waits are the only ones
+    __builtin_amdgcn_s_waitcnt(0);
     if (a.scale < 0.f) {
         // a negative scale is carried by q's sign (exact), so the exponent factor is positive
 #pragma unroll
@@ -221,11 +265,12 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
     float m_run = -INFINITY, l_run = 0.f;  // m in log2 units (scaled score)
     const float cexp = fabsf(a.scale) * kLog2e;
 
-    // LDS read offsets within a tile. K (A operand of 16x16x32): row 16 wave + l % 16, logical
-    // chunk 4 ks + l / 16. V^T (A operand of 16x16x16) by the transposing read: 16-lane group
+    // LDS read offsets within a block's array. K (A operand of 16x16x32): row 16 wave + l % 16,
+    // logical chunk 4 ks + l / 16. V^T (A operand of P.V) by the transposing read: 16-lane group
     // q4 reads rows 16 wave + 4 q4 + j / 4 at dims 16 db + 4 (j & 3) + 0..3 (j = lane % 16),
-    // which gives lane l dim 16 db + l % 16 at keys 4 q4 + 0..3.
-    int koff[KS], voff[DB];
+    // which gives lane l dim 16 db + l % 16 at keys 4 q4 + 0..3; blocks db and db + 8 differ by
+    // 256 bytes
+    int koff[KS], voff[DB / 2];
     {
         const int kr = 16 * wave + c16;
 #pragma unroll
@@ -235,9 +280,9 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
         }
         const int vr = 16 * wave + 4 * q4 + (c16 >> 2);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB / 2; ++db) {
             const int c = 2 * db + ((c16 & 3) >> 1);
-            voff[db] = vr * RB + 16 * ((c & ~15) | ((c & 15) ^ swz(vr))) + 8 * (c16 & 1);
+            voff[db] = vr * RB + 16 * (c ^ swz(vr)) + 8 * (c16 & 1);
         }
     }
 
@@ -251,60 +296,69 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
         return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
     };
 
-    // one quarter of block `tile` from stages kt / vt; the next quarter's loads (descriptors
-    // with no records unless it is on the fast path) go out in between; waits as in
-    // prompt_quarter.h: this quarter's K with all but the last QL loads landed, its V with all
-    // but the next quarter's QL K loads
-    auto quarter = [&](int tile, bool nxt, int ntile, const char* kt, const char* vt, char* kn, char* vn)
-        __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t nrk = qdesc(ntile, kg, nxt), nrv = qdesc(ntile, vg, nxt);
-        char* const nkd = kn + 16 * RB * wave;
-        char* const nvd = vn + 16 * RB * wave;
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);
-        f32x4 s0, s1;
+    // One step over blocks (ta, tb). In flight at its start: this step's V (QL loads a quarter,
+    // plus QL for each edge quarter), then its K (the same). V^T is read first, so that the
+    // next step's V streams in while the score products run (one load after each of them;
+    // descriptors with no records unless on the fast path, edge quarters key by key after
+    // them); the next step's K goes out once the score products have read this step's, one
+    // load after each 16-dim block of P.V (edge quarters after it).
+    for (;;) {
+        lds_dma_wait_vm16();               // this step's V (its K may still be in flight)
+        uint2 vta[DB], vtb[DB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-        Pack8 ka[2];
-        ka[0].u = *reinterpret_cast<const uint4*>(kt + koff[0]);
-        ka[1].u = *reinterpret_cast<const uint4*>(kt + koff[1]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const Pack8 c = ka[ks & 1];
-            if (ks + 2 < KS) ka[ks & 1].u = *reinterpret_cast<const uint4*>(kt + koff[ks + 2]);
-            if (ks & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.v, qreg[ks].v, s1, 0, 0, 0);
-            else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.v, qreg[ks].v, s0, 0, 0, 0);
-            buffer_to_lds16(nrk, nkd + 1024 * ks, lane_off[ks]);
+        for (int db = 0; db < DB; ++db) {
+            const int off = voff[db & 7] + (db >> 3) * 256;
+            vta[db] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vs[0] + off)));
+            vtb[db] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(Vs[1] + off)));
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        lds_wait_reads();                  // V^T read: its stage may be refilled
+        lds_dma_wait_vm0();                // this step's K
+        const bool more = rem != 0;
+        const int na = more ? take() : ta;
+        const bool nhb = rem != 0;
+        const int nb = nhb ? take() : na;
+        const bool fva = more && is_fast(na), fvb = nhb && is_fast(nb);
+        f32x4 sa, sb;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int r = 0; r < 4; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
+        {
+            const __amdgpu_buffer_rsrc_t rva = qdesc(vg, na, fva), rvb = qdesc(vg, nb, fvb);
+            const uint32_t mva = lds_base(Vs[0]), mvb = lds_base(Vs[1]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Pack8 ka, kb;
+                ka.u = *reinterpret_cast<const uint4*>(Ks[0] + koff[ks]);
+                kb.u = *reinterpret_cast<const uint4*>(Ks[1] + koff[ks]);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qreg[ks].v, sa, 0, 0, 0);
+                lds_dma_buffer16(rva, lane_off[ks], mva + 1024 * ks);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.v, qreg[ks].v, sb, 0, 0, 0);
+                lds_dma_buffer16(rvb, lane_off[ks], mvb + 1024 * ks);
+            }
+            if (more && !fva) issue_edge(vg, na, Vs[0]);
+            if (nhb && !fvb) issue_edge(vg, nb, Vs[1]);
+            lds_wait_reads();              // K read: its stage may be refilled
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);          // this quarter's V
-        uint2 vx[DB];
+        // online softmax over keys 16w + 4 q4 + 0..3 of blocks a (x[0..3]) and b (x[4..7])
+        float x[8];
+        {
+            const int kba = ta * BN + 16 * wave + 4 * q4, kbb = tb * BN + 16 * wave + 4 * q4;
+            const bool sela = (eff >> (ta - tb0)) & 1;
+            const bool selb = hb && ((eff >> (tb - tb0)) & 1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            vx[db] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16_ptr)(vt + voff[db])));
-        // online softmax over keys 16w + 4 q4 + 0..3 of this lane's column
-        float x[4];
-        const int kb = tile * BN + 16 * wave + 4 * q4;
-        const bool sel = (eff >> (tile - tb0)) & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = s0[i] + s1[i];
-            if (!sel || kb + i < lo || kb + i > last) x[i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (sela & (kba + i >= lo) & (kba + i <= last)) ? sa[i] : -INFINITY;
+                x[4 + i] = (selb & (kbb + i >= lo) & (kbb + i <= last)) ? sb[i] : -INFINITY;
+            }
         }
-        const float smax = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float smax = col_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
         const float m_cand = fmaxf(m_run, smax * cexp);
         const bool grow = m_cand > m_run + kLazy;
         const float m_new = grow ? m_cand : m_run;
         const float mu = (m_new == -INFINITY) ? 0.f : m_new;
         float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const float p = __builtin_amdgcn_exp2f(fmaf(x[i], cexp, -mu));
             x[i] = p;
             psum += p;
@@ -319,58 +373,46 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
         }
         l_run += psum;
         m_run = m_new;
-        // NP bf16 parts of P (B operand: keys 4 q4 + 0..3 of column l % 16)
-        uint2 phi, pmid, plo;
-        {
-            phi.x = cvt_pk_bf16(x[0], x[1]);
-            phi.y = cvt_pk_bf16(x[2], x[3]);
-            if (NP == 2 && WA_CONTROL == 6) { pmid.x = 0u; pmid.y = 0u; }
-            else if (NP >= 2) {
-                const float e0 = x[0] - lo_bf16(phi.x), e1 = x[1] - hi_bf16(phi.x);
-                const float e2 = x[2] - lo_bf16(phi.y), e3 = x[3] - hi_bf16(phi.y);
-                pmid.x = cvt_pk_bf16(e0, e1);
-                pmid.y = cvt_pk_bf16(e2, e3);
-                if (NP == 3) {
-                    plo.x = cvt_pk_bf16(e0 - lo_bf16(pmid.x), e1 - hi_bf16(pmid.x));
-                    plo.y = cvt_pk_bf16(e2 - lo_bf16(pmid.y), e3 - hi_bf16(pmid.y));
-                }
+        // NP bf16 parts of P: the B operand, keys a 4 q4 + 0..3 then b 4 q4 + 0..3 of column l % 16
+        uint32_t wh[4], wm[4], wl[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            wh[h] = cvt_pk_bf16(x[2 * h], x[2 * h + 1]);
+            wm[h] = wl[h] = 0u;
+            if (NP >= 2 && !(NP == 2 && WA_CONTROL == 6)) {
+                const float e0 = x[2 * h] - lo_bf16(wh[h]), e1 = x[2 * h + 1] - hi_bf16(wh[h]);
+                wm[h] = cvt_pk_bf16(e0, e1);
+                if (NP == 3) wl[h] = cvt_pk_bf16(e0 - lo_bf16(wm[h]), e1 - hi_bf16(wm[h]));
             }
         }
+        Pack8 ph, pm, pl;
+        ph.u = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        pm.u = make_uint4(wm[0], wm[1], wm[2], wm[3]);
+        pl.u = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        const bool fka = more && is_fast(na), fkb = nhb && is_fast(nb);
+        const __amdgpu_buffer_rsrc_t rka = qdesc(kg, na, fka), rkb = qdesc(kg, nb, fkb);
+        const uint32_t mka = lds_base(Ks[0]), mkb = lds_base(Ks[1]);
+        // O^T += V^T P^T: per 16-dim block, the two blocks' V^T side by side as one 32-key operand
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const s16x4 av = __builtin_bit_cast(s16x4, vx[db]);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, phi), oacc[db], 0, 0, 0);
-            if (NP >= 2)
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, pmid), oacc[db], 0, 0, 0);
-            if (NP == 3)
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, plo), oacc[db], 0, 0, 0);
-            if (db & 1) buffer_to_lds16(nrv, nvd + 1024 * (db >> 1), lane_off[db >> 1]);
+            Pack8 av;
+            av.u = make_uint4(vta[db].x, vta[db].y, vtb[db].x, vtb[db].y);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, ph.v, oacc[db], 0, 0, 0);
+            if (NP >= 2) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, pm.v, oacc[db], 0, 0, 0);
+            if (NP == 3) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, pl.v, oacc[db], 0, 0, 0);
+            if (db < QL) lds_dma_buffer16(rka, lane_off[db], mka + 1024 * db);
+            else lds_dma_buffer16(rkb, lane_off[db - QL], mkb + 1024 * (db - QL));
         }
-#pragma unroll
-        for (int db = 0; db < DB; db += 2) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NP, 1);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-        }
-    };
-
-    // walk the selected blocks in ascending order, two at a time over fixed stage arrays
-    auto step = [&](const char* kt, const char* vt, char* kn, char* vn) __attribute__((always_inline)) {
-        const bool more = rem != 0;
-        const int nxt = more ? tb0 + ctz64(rem) : cur;
-        const bool fast = more && is_fast(nxt);
-        quarter(cur, fast, nxt, kt, vt, kn, vn);
-        if (more && !fast) issue_edge(nxt, kn, vn);
-        rem &= rem - 1;
-        cur = nxt;
-        return more;
-    };
-    for (;;) {
-        if (!step(Ks0, Vs0, Ks1, Vs1)) break;
-        if (!step(Ks1, Vs1, Ks0, Vs0)) break;
+        if (more && !fka) issue_edge(kg, na, Ks[0]);
+        if (nhb && !fkb) issue_edge(kg, nb, Ks[1]);
+        if (!more) break;
+        ta = na;
+        tb = nb;
+        hb = nhb;
     }
 
-    // merge of the four quarters' states: wave w stores its O into its own rows of Ks0 (dims
-    // 0..127) and Vs0 (dims 128..255), column-major rows of 128 floats, the 16-byte chunk c of
+    // merge of the four quarters' states: wave w stores its O into its own rows of Ks[0] (dims
+    // 0..127) and Ks[1] (dims 128..255), column-major rows of 128 floats, the 16-byte chunk c of
     // column p at c ^ (p & 15)
     const float l_tot = col_sum(l_run);
     __builtin_amdgcn_s_waitcnt(0);
@@ -378,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
     for (int db = 0; db < DB; ++db) {
         const int d0 = 16 * db + 4 * q4;                  // dims d0 .. d0 + 3
         const int c = (d0 & 127) >> 2;
-        float* ob = reinterpret_cast<float*>((d0 < 128 ? Ks0 : Vs0) + 16 * RB * wave) + c16 * 128;
+        float* ob = reinterpret_cast<float*>(Ks[d0 < 128 ? 0 : 1] + 16 * RB * wave) + c16 * 128;
         *reinterpret_cast<float4*>(ob + 4 * (c ^ c16)) =
             make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
     }
@@ -397,8 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
         ac[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         lsum = fmaf(ac[w], red_l[w][c16], lsum);
     }
-    const int pos = __builtin_amdgcn_readfirstlane(wave);
-    const char* const half = pos < 2 ? Ks0 : Vs0;         // dims 64w.. lie in this array
+    const char* const half = Ks[wave < 2 ? 0 : 1];        // dims 64w.. lie in this array
     const int64_t pi = ((int64_t)row * a.hq + head) * a.Cp + (seg - lo / kSparseSeg);
     if (q4 == 0) { a.pm[pi] = M; a.pl[pi] = lsum; }
     float* op = a.po + pi * D + 64 * wave + 16 * q4;

@@ -205,6 +205,7 @@ int wa_prompt(const wa_window_t* w,
     a.k = k; a.v = v; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
     a.p0 = p0; a.n = n; a.hq = hq; a.hkv = hkv; a.d = d;
     a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p_parts = 1 + w->p32;
+    a.ring_magic = wa::mod_magic((uint32_t)w->ring);
     a.hi = hi;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
     a.nchunk = 1; a.Cp = 0; a.chunk_keys = wa::kPromptChunk; a.pm = a.pl = a.po = nullptr;
@@ -263,6 +264,7 @@ int wa_prompt_sparse(const wa_window_t* w,
     a.k = k; a.v = v; a.kv_sslot = kv_sslot; a.kv_shead = kv_shead;
     a.p0 = p0; a.n = n; a.hq = hq; a.hkv = hkv; a.d = d;
     a.window = w->window; a.ring = w->ring; a.scale = w->scale; a.p_parts = 1 + w->p32;
+    a.ring_magic = wa::mod_magic((uint32_t)w->ring);
     a.hi = hi;
     a.out = out; a.o_srow = o_srow; a.o_shead = o_shead;
     a.bm = blocks; a.bm_srow = blocks_srow; a.bm_words = blocks_words;

@@ -57,11 +57,21 @@ struct DecodeArgs {
     uint16_t* out; int64_t o_srow, o_shead;
 };
 
+// x mod d for a 32-bit unsigned x and 1 <= d < 2^32, from M = floor((2^64 - 1) / d) + 1
+// computed once: the high 64 bits of (M x mod 2^64) times d (direct remainder: Lemire, Kaser
+// and Kurz, "Faster remainder by direct computation", 2019, exact for every such x and d). A
+// division by a value only known at run time costs a long chain of VALU instructions.
+inline uint64_t mod_magic(uint32_t d) { return ~0ull / d + 1; }
+__device__ __forceinline__ int mod_by_magic(int x, uint64_t M, int d) {
+    return (int)__umul64hi(M * (uint32_t)x, (uint64_t)(uint32_t)d);
+}
+
 struct PromptArgs {
     const uint16_t* q; int64_t q_srow, q_shead;
     const uint16_t* k; const uint16_t* v; int64_t kv_sslot, kv_shead;
     int32_t p0, n, hq, hkv, d;
     int32_t window, ring; float scale;
+    uint64_t ring_magic;          // mod_magic(ring): ring slots of key positions by ring_slot
     int32_t p_parts;              // bf16 parts carrying P into P.V: 1, 2 (p32) or 3
     const int32_t* hi;
     uint16_t* out; int64_t o_srow, o_shead;
@@ -75,6 +85,10 @@ struct PromptArgs {
     // selected); bm == nullptr: every key of the range
     const uint32_t* bm; int64_t bm_srow; int32_t bm_words;
 };
+
+// ring slot of key position x >= 0 of a prompt
+__device__ __forceinline__ int ring_slot(const PromptArgs& a, int x) { return mod_by_magic(x, a.ring_magic, a.ring); }
+
 
 constexpr int kSparseBlock = 64;   // keys per selectable block (= the prompt kernel's key tile)
 
