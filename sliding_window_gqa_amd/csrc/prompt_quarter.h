@@ -130,18 +130,22 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         char* kd;
         char* vd;
     };
-    auto prep = [&](int tile, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
+    // a quarter whose first key's ring slot sq and element offset so = sq * kv_sslot are known
+    auto prep_at = [&](int tile, int sq, int64_t so, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
         QLoad L;
         L.qb = tile * BN + 16 * wave;
-        L.sq = ring_slot(a, L.qb);
+        L.sq = sq;
         L.kcap = kcap;
         L.kd = kdst + 16 * RB * wave;
         L.vd = vdst + 16 * RB * wave;
         L.fast = L.qb >= kmin && L.qb + 15 <= kcap && L.sq + 16 <= a.ring;
-        const int64_t so = (int64_t)L.sq * a.kv_sslot;
         L.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + so), (short)0, quarter_extent, 0x00020000);
         L.rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + so), (short)0, quarter_extent, 0x00020000);
         return L;
+    };
+    auto prep = [&](int tile, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
+        const int sq = ring_slot(a, tile * BN + 16 * wave);
+        return prep_at(tile, sq, (int64_t)sq * a.kv_sslot, kdst, vdst, kcap);
     };
     // wave load i of K (v = false) or V (v = true) of a prepared quarter
     auto part = [&](const QLoad& L, int i, bool v) __attribute__((always_inline)) {
@@ -255,15 +259,12 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     // issued inside, one after each 32-dim step of the score products (K) and one after each
     // 32-dim block of P.V (V): the load path takes one at a time while the products run,
     // instead of the wave stalling on a batch. nxt: the next quarter is on the fast path.
-    auto quarter = [&](bool nxt, int tile, const char* kt, const char* vt, char* knext, char* vnext)
+    auto quarter = [&](bool nxt, int64_t nso, int tile, const char* kt, const char* vt, char* knext, char* vnext)
         __attribute__((always_inline)) {
-        // descriptors of the next quarter's K and V: with no records when it is not on the
-        // fast path (those loads then touch no memory), so that every quarter issues the same
-        // loads at the same places and waits the same way
-        const int nqb = (tile + 1) * BN + 16 * wave;
-        const int nsq = ring_slot(a, nqb);
+        // descriptors of the next quarter's K and V (element offset nso of its first slot):
+        // with no records when it is not on the fast path (those loads then touch no memory),
+        // so that every quarter issues the same loads at the same places and waits the same way
         const int nrec = nxt ? quarter_extent : 0;
-        const int64_t nso = (int64_t)nsq * a.kv_sslot;
         const __amdgpu_buffer_rsrc_t nrk = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + nso), (short)0, nrec, 0x00020000);
         const __amdgpu_buffer_rsrc_t nrv = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + nso), (short)0, nrec, 0x00020000);
         char* const nkd = knext + 16 * RB * wave;
@@ -383,12 +384,25 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     // quarter loads the next quarter on the fast path itself; an edge next quarter (the ends
     // of the range, a ring wrap), or the next quarter of a tile this wave skips, is issued
     // whole afterwards
+    //
+    // ns, nso: ring slot and element offset of this wave's quarter of the tile after the
+    // current one, advanced a tile at a time (one wrap per tile in a ring of at least 64
+    // slots, a loop in a shorter one) instead of a remainder and a product per tile
+    int ns = ring_slot(a, (t0 + 1) * BN + 16 * wave);
+    int64_t nso = (int64_t)ns * a.kv_sslot;
+    const int64_t tile_elems = (int64_t)BN * a.kv_sslot, ring_elems = (int64_t)a.ring * a.kv_sslot;
     auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more) {
         const bool nxt = more && meets(tile + 1);
-        const bool fast = nxt && prep(tile + 1, knext, vnext, kmax).fast;
+        const bool fast = nxt && prep_at(tile + 1, ns, nso, knext, vnext, kmax).fast;
         const bool here = meets(tile);
-        if (here) quarter(fast, tile, kt, vt, knext, vnext);
-        if (nxt && !(here && fast)) issue_all(prep(tile + 1, knext, vnext, kmax));
+        if (here) quarter(fast, nso, tile, kt, vt, knext, vnext);
+        if (nxt && !(here && fast)) issue_all(prep_at(tile + 1, ns, nso, knext, vnext, kmax));
+        ns += BN;
+        nso += tile_elems;
+        while (ns >= a.ring) {
+            ns -= a.ring;
+            nso -= ring_elems;
+        }
     };
 
     if (a.scale < 0.f) {
