@@ -6,29 +6,33 @@
 // positions, every tile folds into a running (m, l, O) with one rescale, P enters P.V as one
 // bf16, as bf16(P) + bf16(P - bf16(P)) (p32), or as three bf16 parts.
 //
-// Design (own): a workgroup holds 32 (row, query head) pairs of one key head and four waves,
-// one per SIMD. All four waves hold the same 32 pairs; they share every 64-key K/V tile in
-// LDS and wave w takes the keys 16w .. 16w + 15 of each tile (its quarter), with a running
-// (m, l, O) of its own over its quarters. After the last tile the four states are merged in
-// LDS in wave order: M = max m_w, a_w = 2^(m_w - M), den = sum a_w l_w, out =
-// bf16(sum (a_w / den) O_w), the sums fma chains in w order. So every row is finished inside its workgroup: no fp32
+// Design (own): a workgroup holds 32 (row, query head) pairs of one key head and eight waves,
+// two per SIMD. Wave w takes the keys 16 (w % 4) .. + 15 (its quarter) of the even tiles
+// (absolute index) of the block's key range (w < 4) or of the odd ones (w >= 4), with a
+// running (m, l, O) of its
+// own; the two waves of a SIMD work on different tiles, so one's softmax runs while the
+// other's matrix products do. After the last tile the eight states are merged in LDS: each
+// odd-tile wave into the even-tile wave of the same quarter, then the four in quarter order
+// (M = max m_w, a_w = 2^(m_w - M), den = sum a_w l_w, out = bf16(sum (a_w / den) O_w), the
+// sums fma chains in w order). So every row is finished inside its workgroup: no fp32
 // partials leave the CU and no merge kernel follows; a (row, head) whose bf16 output is not
 // finite is re-run in float64 by the same workgroup (rerun_f64.h), so no check kernel
-// follows either. A row's bits depend only on its key
-// range and the absolute tile grid (a quarter holding none of the row's keys leaves that
-// row's state exactly unchanged), never on how the prompt is cut into calls.
+// follows either. A row's bits depend only on its key range and the absolute tile grid (a
+// quarter holding none of the row's keys leaves that row's state exactly unchanged), never on
+// how the prompt is cut into calls.
 //   * S^T of a quarter (16 keys x 32 pairs) is two v_mfma_f32_16x16x32_bf16 chains (pairs
-//     0..15 and 16..31) over eight 32-dim steps; K fragments are 16-byte LDS reads, the Q^T
-//     operand stays in registers for the whole walk;
+//     0..15 and 16..31) over eight 32-dim steps; K fragments are 16-byte LDS reads of the
+//     wave's own rows, the Q^T operand 16-byte reads of the block's q, stored once in LDS;
 //   * one v_permlane16_swap per accumulator register moves the scores into the layout of
 //     the P^T operand of v_mfma_f32_32x32x16_bf16: lane l then holds pair l % 32 and keys
 //     8 (l / 32) .. + 7 of the quarter, so the mask, the row maximum (one v_permlane32_swap
-//     between the two lane halves), the exponentials and the O rescale are lane-local, as in
-//     the 128-pair kernel;
+//     between the two lane halves), the exponentials and the O rescale are lane-local;
 //   * O^T += V^T P^T over the quarter's 16 keys: eight 32-dim blocks, NP MFMAs each, V^T from
 //     the transposing LDS read (ds_read_b64_tr_b16);
-//   * tiles are fetched by buffer loads straight into double-buffered LDS (one barrier a
-//     tile), with the 16-byte-chunk swizzle and the ring wrap of the 128-pair kernel;
+//   * each wave loads only its own 16 rows of K and V (no barrier in the walk) into one
+//     stage per tile parity, by LDS-direct loads with explicit waits: V^T is read first, the
+//     next quarter's V streams in during the score products and its K during P.V; 16-byte
+//     chunks swizzled against bank conflicts, ring wrap as in the 128-pair kernel;
 //   * workgroup ids are remapped so that each XCD walks a contiguous range of (key head,
 //     block of pairs), keeping a key head's K/V stream in its L2.
 // Against the 128-pair kernel this spreads one block of pairs over all four SIMDs of a CU
@@ -53,8 +57,37 @@ constexpr int kWaitVm16 = 0x4000 | 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
 constexpr int kWaitVm0 = 0x0F70;
 
+
+constexpr int kOctWaves = 8;           // waves of a quarter-tile workgroup (two per SIMD)
+constexpr int kOctThreads = 64 * kOctWaves;
+
+// LDS loads issued as inline assembly (they write LDS only, no register): the compiler does not
+// track them, so each wait on them is written out (lds_dma_wait_*, s_waitcnt before the results
+// are read). M0 holds the wave's LDS destination; lane i's 16 bytes land at M0 + 16 i.
+// Volatile statements keep their order among themselves; the waits below also order every
+// memory access around them, so an LDS read and the load that refills its stage stay on either
+// side of a wait.
+__device__ __forceinline__ void lds_dma_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(m0), "s"(rsrc));
+}
+__device__ __forceinline__ void lds_dma_global16(const void* src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0));
+}
+// all but the last 16 (8) vector-memory loads have landed; all have
+__device__ __forceinline__ void lds_dma_wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void lds_dma_wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void lds_dma_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// every LDS read issued so far has returned
+__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// LDS address of a shared-memory pointer, uniform over the wave
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_ptr)p);
+}
+
 template <int NP>
-__global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs a, int nblk) {
+__global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptArgs a, int nblk) {
     constexpr int D = 256;
     constexpr int KS = D / 32;             // 32-dim steps of S^T
     constexpr int DBLK = D / 32;           // 32-dim blocks of O^T
@@ -62,15 +95,16 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     constexpr int RPK = 1024 / RB;         // rows per 1 KiB wave load
     constexpr int TILE_B = BN * RB;        // bytes of one K (or V) tile
-    // two stages of K and V tiles (distinct arrays: the compiler can tell the direct-to-LDS
-    // loads into one stage from the reads of the other); after the walk wave w's O goes to
-    // array w (32 pairs x 256 dims x 4 bytes = one tile)
-    __shared__ __attribute__((aligned(1024))) char Ks0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Vs0[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Ks1[TILE_B];
-    __shared__ __attribute__((aligned(1024))) char Vs1[TILE_B];
-    __shared__ float red_m[kWaves][kQuarterPairs];
-    __shared__ float red_l[kWaves][kQuarterPairs];
+    constexpr int QL = 16 * RB / 1024;     // wave loads per quarter (each of K and V)
+    static_assert(QL == KS && QL == DBLK, "one V load per score step, one K load per O block");
+    // one stage per tile parity (K and V: 32 KiB each); wave w owns rows 16 (w % 4) .. + 15
+    // of its parity's stage. After the walk these four arrays hold the O of the merge.
+    __shared__ __attribute__((aligned(1024))) char Ks[2][TILE_B];
+    __shared__ __attribute__((aligned(1024))) char Vs[2][TILE_B];
+    // Q^T operand: pair p's 256 dims in 512 bytes, 16-byte chunk c at c ^ (p & 15)
+    __shared__ __attribute__((aligned(1024))) char Qs[kQuarterPairs * RB];
+    __shared__ float red_m[kOctWaves][kQuarterPairs];
+    __shared__ float red_l[kOctWaves][kQuarterPairs];
     __shared__ int bad[kQuarterPairs];     // pairs whose bf16 output holds a NaN or an infinity
 
     // XCD x (ids dealt out to the 8 XCDs in turn) takes a contiguous share of the logical
@@ -86,8 +120,11 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     if (tid < kQuarterPairs) bad[tid] = 0;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: quarter addresses
+    const int qw = wave & 3;               // quarter of the tile
+    const int par = wave >> 2;             // tile parity
     const int h = lane >> 5;               // lane half: keys 8h .. 8h + 7 of a quarter
     const int col = lane & 31;             // pair of the P^T / O^T layout
+    const int c16 = lane & 15, q4 = lane >> 4;
     const int G = a.hq / a.hkv;
 
     const int pair = blk * kQuarterPairs + col;
@@ -95,25 +132,29 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     const int head = g * G + pair % G;
     const bool valid = row < a.n;
 
-    // The block's key range before hi is known: lo is non-decreasing in the row, so the first
-    // valid row gives kmin; every valid row's last key is at least its own position, so the
-    // last valid row's position is a lower bound of kmax.
+    // the block's key range: lo is non-decreasing in the row, so the first valid row gives
+    // kmin; kmax is the largest last key of a valid pair
     const int row_first = blk * kQuarterPairs / G;
-    const int row_last = min(a.n - 1, (blk * kQuarterPairs + kQuarterPairs - 1) / G);
-    const bool any_valid = row_first < a.n;
+    if (row_first >= a.n) return;          // no valid pair in this workgroup (uniform)
     const int kmin = prompt_lo(a, row_first);
-    const int kmax_low = a.p0 + row_last;
+    const int big = 0x7FFFFFFF;
+    int lo = big, last = -1;               // empty range for padding pairs
+    if (valid) prompt_span(a, row, lo, last);
+    // every wave holds the same 32 pairs, so these are the workgroup's values as well; kept in
+    // scalar registers so that the tile addresses and descriptors derived from them are too
+    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(last));
+    const int loall = __builtin_amdgcn_readfirstlane(wave_max_i(valid ? lo : -1));
+    const int lastall = __builtin_amdgcn_readfirstlane(wave_min_i(valid ? last : big));
+    const int t0 = kmin / BN, t1 = kmax / BN;
 
     const uint16_t* kg = a.k + (int64_t)g * a.kv_shead;
     const uint16_t* vg = a.v + (int64_t)g * a.kv_shead;
 
-    // Tile loads: wave w loads only its own quarter, rows 16w .. 16w + 15 of K and V (the rows
-    // no other wave reads), as QL 1 KiB wave loads each (RPK rows of CPR chunks), K's before
-    // V's. A quarter with every key inside [kmin, kcap] and no ring wrap goes by buffer loads
-    // from a descriptor on its first slot; an edge quarter key by key, clamped into
-    // [kmin, kcap] (keys the ring holds; keys outside a row's range are masked) and wrapped
-    // into the ring.
-    constexpr int QL = 16 * RB / 1024;     // wave loads per quarter (each of K and V)
+    // Tile loads: a wave loads only its own quarter, QL 1 KiB wave loads each of K and V (RPK
+    // rows of CPR chunks). A quarter with every key inside [kmin, kmax] and no ring wrap goes
+    // by buffer loads from a descriptor on its first slot (no records: zeros); an edge quarter
+    // key by key, clamped into [kmin, kmax] (keys outside a pair's range are masked) and
+    // wrapped into the ring. Every quarter issues QL loads each.
     const int ld_row = lane / CPR, ld_p = lane % CPR;
     uint32_t lane_off[QL];
 #pragma unroll
@@ -123,100 +164,97 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         lane_off[i] = (uint32_t)(r * a.kv_sslot + 8 * c) * 2u;
     }
     const int quarter_extent = (int)((uint32_t)(15 * a.kv_sslot) * 2u + 2u * D);
-    struct QLoad {
-        bool fast;
-        __amdgpu_buffer_rsrc_t rk, rv;
-        int qb, sq, kcap;
-        char* kd;
-        char* vd;
+    char* const kst = Ks[par] + 16 * RB * qw;              // this wave's rows of its stage
+    char* const vst = Vs[par] + 16 * RB * qw;
+    const uint32_t mk = lds_addr(kst), mv = lds_addr(vst);
+    // quarter of tile `tile` whose first key sits in ring slot sq (element offset so)
+    auto is_fast = [&](int tile, int sq) __attribute__((always_inline)) {
+        const int qb = tile * BN + 16 * qw;
+        return qb >= kmin && qb + 15 <= kmax && sq + 16 <= a.ring;
     };
-    // a quarter whose first key's ring slot sq and element offset so = sq * kv_sslot are known
-    auto prep_at = [&](int tile, int sq, int64_t so, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
-        QLoad L;
-        L.qb = tile * BN + 16 * wave;
-        L.sq = sq;
-        L.kcap = kcap;
-        L.kd = kdst + 16 * RB * wave;
-        L.vd = vdst + 16 * RB * wave;
-        L.fast = L.qb >= kmin && L.qb + 15 <= kcap && L.sq + 16 <= a.ring;
-        L.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + so), (short)0, quarter_extent, 0x00020000);
-        L.rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + so), (short)0, quarter_extent, 0x00020000);
-        return L;
+    auto qdesc = [&](const uint16_t* src, int64_t so, bool use) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(src + so), (short)0, use ? quarter_extent : 0, 0x00020000);
     };
-    auto prep = [&](int tile, char* kdst, char* vdst, int kcap) __attribute__((always_inline)) {
-        const int sq = ring_slot(a, tile * BN + 16 * wave);
-        return prep_at(tile, sq, (int64_t)sq * a.kv_sslot, kdst, vdst, kcap);
-    };
-    // wave load i of K (v = false) or V (v = true) of a prepared quarter
-    auto part = [&](const QLoad& L, int i, bool v) __attribute__((always_inline)) {
-        char* const dst = (v ? L.vd : L.kd) + 1024 * i;
-        if (L.fast) {
-            buffer_to_lds16(v ? L.rv : L.rk, dst, lane_off[i]);
-            return;
+    // key qb + r clamped into [kmin, kmax] and wrapped into the ring, counted from the
+    // quarter's first key clamped into that range (every clamped key lies 0 .. 15 keys after
+    // it: one wrap at most in a ring of at least 16 slots)
+    auto issue_edge = [&](const uint16_t* src, int tile, uint32_t m0) __attribute__((always_inline)) {
+        const int qb = tile * BN + 16 * qw;
+        const int qbc = min(max(qb, kmin), kmax);
+        const int sqc = ring_slot(a, qbc);
+#pragma unroll
+        for (int i = 0; i < QL; ++i) {
+            const int r = RPK * i + ld_row;
+            const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
+            const int jc = min(max(qb + r, kmin), kmax);
+            int slot = sqc + (jc - qbc);
+            if (a.ring >= 16) slot = slot >= a.ring ? slot - a.ring : slot;
+            else slot = jc % a.ring;
+            lds_dma_global16(src + (int64_t)slot * a.kv_sslot + 8 * c, m0 + 1024 * i);
         }
-        const int r = RPK * i + ld_row;
-        const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
-        const int jc = min(max(L.qb + r, kmin), L.kcap);
-        // jc - qb < 16: a ring of at least 16 slots wraps at most once inside a quarter, a
-        // shorter ring may wrap several times
-        int slot = L.sq + (jc - L.qb);
-        if (a.ring >= 16) slot = slot >= a.ring ? slot - a.ring : slot;
-        else slot = jc % a.ring;
-        __builtin_amdgcn_global_load_lds((v ? vg : kg) + (int64_t)slot * a.kv_sslot + 8 * c,
-                                         (lds_void_ptr)dst, 16, 0, 0);
     };
-    static_assert(QL == KS && QL == DBLK, "one K load per score step, one V load per O block");
-    auto issue_all = [&](const QLoad& L) __attribute__((always_inline)) {
+    auto issue_whole = [&](const uint16_t* src, int tile, int sq, int64_t so, uint32_t m0) __attribute__((always_inline)) {
+        if (is_fast(tile, sq)) {
+            const __amdgpu_buffer_rsrc_t rs = qdesc(src, so, true);
 #pragma unroll
-        for (int i = 0; i < QL; ++i) part(L, i, false);
-#pragma unroll
-        for (int i = 0; i < QL; ++i) part(L, i, true);
+            for (int i = 0; i < QL; ++i) lds_dma_buffer16(rs, lane_off[i], m0 + 1024 * i);
+        } else {
+            issue_edge(src, tile, m0);
+        }
     };
 
-    // hi (if any) is loaded first, then this wave's first quarter when it lies below kmax_low
-    // (so it needs no hi), then q: the three latencies overlap
-    const int big = 0x7FFFFFFF;
-    int lo = big, last = -1;               // empty range for padding pairs
-    if (valid) prompt_span(a, row, lo, last);
-    const int t0 = kmin / BN;
-    const int qb0 = t0 * BN + 16 * wave;
-    const bool early = any_valid && qb0 + 15 >= kmin && qb0 + 15 <= kmax_low;
-    if (early) issue_all(prep(t0, Ks0, Vs0, kmax_low));
-
-    // Q^T operand of the 16x16x32 products: lane l holds pair 16 nb + l % 16 at dims
-    // 32 ks + 8 (l / 16) + 0..7; a padding pair takes row 0's q (its column of S^T is never
-    // used: its range is empty, so every key is masked)
-    Pack8 qreg[2][KS];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int pr = blk * kQuarterPairs + 16 * nb + (lane & 15);
-        const int qrow = pr / G;
-        const uint16_t* qp = a.q + (int64_t)(qrow < a.n ? qrow : 0) * a.q_srow +
-                             (int64_t)(g * G + pr % G) * a.q_shead + 8 * (lane >> 4);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[nb][ks].u = *reinterpret_cast<const uint4*>(qp + 32 * ks);
-    }
-
-    // every wave holds the same 32 pairs, so these are the workgroup's values as well; they
-    // are the same on every lane, and kept in scalar registers so that the tile addresses and
-    // buffer descriptors derived from them are scalar too
-    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(last));
-    if (!any_valid) return;                // no valid pair in this workgroup (uniform, no loads)
-    const int loall = __builtin_amdgcn_readfirstlane(wave_max_i(valid ? lo : -1));
-    const int lastall = __builtin_amdgcn_readfirstlane(wave_min_i(valid ? last : big));
-    const int t1 = kmax / BN;
-
-    // this wave's quarter of a tile: does it meet the workgroup's keys, and does every valid
-    // pair see all of it (no mask)?
+    // this wave's tiles: those of its parity (absolute tile index, so that a row's bits do not
+    // depend on where a call's first block starts) that its quarter meets (keys of the
+    // block's range), a contiguous run ta, ta + 2, .., tz
     auto meets = [&](int tile) __attribute__((always_inline)) {
-        const int qb = tile * BN + 16 * wave;
+        const int qb = tile * BN + 16 * qw;
         return qb <= kmax && qb + 15 >= kmin;
     };
     auto is_full = [&](int tile) __attribute__((always_inline)) {
-        const int qb = tile * BN + 16 * wave;
+        const int qb = tile * BN + 16 * qw;
         return qb >= loall && qb + 15 <= lastall;
     };
-    if (!early && meets(t0)) issue_all(prep(t0, Ks0, Vs0, kmax));
+    int ta = t0 + ((par - t0) & 1);
+    if (ta <= t1 && !meets(ta)) ta += 2;
+    int tz = t1 - ((t1 - par) & 1);                    // last tile of this parity
+    if (tz >= ta && !meets(tz)) tz -= 2;
+    const bool work = ta <= tz;
+    // ring slot and element offset of the wave's current quarter, advanced two tiles at a
+    // time (one wrap in a ring of at least 128 slots, a loop in a shorter one)
+    int cs = ring_slot(a, ta * BN + 16 * qw);
+    int64_t cso = (int64_t)cs * a.kv_sslot;
+    const int64_t step_elems = (int64_t)(2 * BN) * a.kv_sslot, ring_elems = (int64_t)a.ring * a.kv_sslot;
+    auto advance = [&](int& sq, int64_t& so) __attribute__((always_inline)) {
+        sq += 2 * BN;
+        so += step_elems;
+        while (sq >= a.ring) {
+            sq -= a.ring;
+            so -= ring_elems;
+        }
+    };
+    if (work) {                            // the first quarter: V, then K
+        issue_whole(vg, ta, cs, cso, mv);
+        issue_whole(kg, ta, cs, cso, mk);
+    }
+
+    // the block's q into LDS (a padding pair takes row 0's q: its range is empty, so every key
+    // is masked); a negative scale is carried by q's sign (exact), so the exponent factor is
+    // positive
+    {
+        const uint32_t sgn = a.scale < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+        for (int k = 0; k < kQuarterPairs * CPR / kOctThreads; ++k) {
+            const int i = tid + kOctThreads * k;
+            const int p = i / CPR, c = i % CPR;
+            const int pr = blk * kQuarterPairs + p;
+            const int qrow = pr / G;
+            const uint4 v = *reinterpret_cast<const uint4*>(
+                a.q + (int64_t)(qrow < a.n ? qrow : 0) * a.q_srow + (int64_t)(g * G + pr % G) * a.q_shead + 8 * c);
+            *reinterpret_cast<uint4*>(Qs + p * RB + 16 * ((c & ~15) | ((c & 15) ^ (p & 15)))) =
+                make_uint4(v.x ^ sgn, v.y ^ sgn, v.z ^ sgn, v.w ^ sgn);
+        }
+    }
+    __syncthreads();
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -226,84 +264,77 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
     float m_run = -INFINITY, l_run = 0.f;  // m in log2 units (scaled score)
     const float cexp = fabsf(a.scale) * kLog2e;
 
-    // LDS read offsets within a tile, fixed for the walk.
-    // K (A operand of 16x16x32): row 16 wave + l % 16, logical chunk 4 ks + l / 16.
-    int koff[KS];
-    {
-        const int kr = 16 * wave + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c = 4 * ks + (lane >> 4);
-            koff[ks] = kr * RB + 16 * ((c & ~15) | ((c & 15) ^ swz(kr)));
-        }
-    }
+    // LDS read offsets, fixed for the walk (the second half of a row's chunks, 256 bytes on).
+    // K (A operand of 16x16x32): own row 16 qw + l % 16, logical chunk 4 ks + l / 16.
+    // Q^T (B operand): pair 16 nb + l % 16 (nb: 16 pairs, 8 KiB on), the same chunk.
     // V^T (A operand of 32x32x16) by the transposing read: 16-lane group q = lane / 16,
-    // j = lane % 16 reads row 16 wave + 8h + 4u + j / 4 at dims 32 db + 16 (q & 1) + 4 (j & 3)
+    // j = lane % 16 reads row 16 qw + 8h + 4u + j / 4 at dims 32 db + 16 (q & 1) + 4 (j & 3)
     // + 0..3; the two reads (u = 0, 1) give lane l dim 32 db + l % 32 at keys 8h + 0..7.
-    int voff[2][DBLK];
+    int koff[KS / 2], qoff[KS / 2], voff[2][DBLK / 2];
     {
+        const int kr = 16 * qw + c16;
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks) {
+            const int c = 4 * ks + q4;
+            koff[ks] = kr * RB + 16 * (c ^ swz(kr));
+            qoff[ks] = c16 * RB + 16 * (c ^ c16);
+        }
         const int j16 = lane & 15, cg = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int vr = 16 * wave + 8 * h + 4 * u + (j16 >> 2);
+            const int vr = 16 * qw + 8 * h + 4 * u + (j16 >> 2);
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
+            for (int db = 0; db < DBLK / 2; ++db) {
                 const int c = 4 * db + cg;
-                voff[u][db] = vr * RB + 16 * ((c & ~15) | ((c & 15) ^ swz(vr))) + 8 * (j16 & 1);
+                voff[u][db] = vr * RB + 16 * (c ^ swz(vr)) + 8 * (j16 & 1);
             }
         }
     }
 
-    // one quarter: S^T, softmax, O^T += V^T P^T. On entry this quarter's QL K and QL V loads
-    // may be in flight (K's first) and nothing after them. The next quarter's loads are
-    // issued inside, one after each 32-dim step of the score products (K) and one after each
-    // 32-dim block of P.V (V): the load path takes one at a time while the products run,
-    // instead of the wave stalling on a batch. nxt: the next quarter is on the fast path.
-    auto quarter = [&](bool nxt, int64_t nso, int tile, const char* kt, const char* vt, char* knext, char* vnext)
-        __attribute__((always_inline)) {
-        // descriptors of the next quarter's K and V (element offset nso of its first slot):
-        // with no records when it is not on the fast path (those loads then touch no memory),
-        // so that every quarter issues the same loads at the same places and waits the same way
-        const int nrec = nxt ? quarter_extent : 0;
-        const __amdgpu_buffer_rsrc_t nrk = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + nso), (short)0, nrec, 0x00020000);
-        const __amdgpu_buffer_rsrc_t nrv = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + nso), (short)0, nrec, 0x00020000);
-        char* const nkd = knext + 16 * RB * wave;
-        char* const nvd = vnext + 16 * RB * wave;
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);          // this quarter's K (its V may fly)
-        // S^T = K Q^T, 16 keys x 32 pairs; K fragments two steps ahead
-        f32x4 s[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[nb][r] = 0.f;
-        Pack8 ka[2];
-        ka[0].u = *reinterpret_cast<const uint4*>(kt + koff[0]);
-        ka[1].u = *reinterpret_cast<const uint4*>(kt + koff[1]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const Pack8 cur = ka[ks & 1];
-            if (ks + 2 < KS) ka[ks & 1].u = *reinterpret_cast<const uint4*>(kt + koff[ks + 2]);
-            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.v, qreg[0][ks].v, s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.v, qreg[1][ks].v, s[1], 0, 0, 0);
-            buffer_to_lds16(nrk, nkd + 1024 * ks, lane_off[ks]);   // next quarter's K
-        }
-        // keep that order: the first two K reads, then per step two products, the next K read
-        // and one load of the next quarter
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);          // this quarter's V
+    // The walk: one quarter a tile. In flight at a quarter's start: its V (QL loads, plus QL
+    // for an edge quarter), then its K (the same). V^T is read first; the next quarter's V
+    // goes out during the score products (one load after each 32-dim step), its K during P.V
+    // (one after each 32-dim block); descriptors with no records unless on the fast path,
+    // edge quarters key by key after them.
+    for (int tile = ta; work; tile += 2) {
+        const bool more = tile + 2 <= tz;
+        int ns = cs;
+        int64_t nso = cso;
+        advance(ns, nso);
+        const bool nfast = more && is_fast(tile + 2, ns);
+
+        lds_dma_wait_vm8();                // this quarter's V (its K may still be in flight)
         uint2 vx[DBLK][2];
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 vx[db][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16_ptr)(vt + voff[u][db])));
+                    (lds_v4i16_ptr)(Vs[par] + voff[u][db & 3] + (db >> 2) * 256)));
+        lds_wait_reads();                  // V^T read: the stage may be refilled
+        lds_dma_wait_vm0();                // this quarter's K
+        // S^T = K Q^T, 16 keys x 32 pairs; the next quarter's V in between
+        f32x4 s[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[nb][r] = 0.f;
+        {
+            const __amdgpu_buffer_rsrc_t nrv = qdesc(vg, nso, nfast);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Pack8 kf, qa, qb;
+                const int ko = koff[ks & 3] + (ks >> 2) * 256, qo = qoff[ks & 3] + (ks >> 2) * 256;
+                kf.u = *reinterpret_cast<const uint4*>(Ks[par] + ko);
+                qa.u = *reinterpret_cast<const uint4*>(Qs + qo);
+                qb.u = *reinterpret_cast<const uint4*>(Qs + 16 * RB + qo);
+                s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qa.v, s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qb.v, s[1], 0, 0, 0);
+                lds_dma_buffer16(nrv, lane_off[ks], mv + 1024 * ks);
+            }
+            if (more && !nfast) issue_edge(vg, tile + 2, mv);
+        }
+        lds_wait_reads();                  // K read: the stage may be refilled
         // to the P^T layout: lane l = 32a + 16b + c holds pair 16b + c; its keys 8a + i come
         // from lane 32a + c (register s[b][i]) and keys 8a + 4 + i from lane 32a + 16 + c
         float x[8];
@@ -313,9 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
             x[i] = __uint_as_float(r[0]);
             x[4 + i] = __uint_as_float(r[1]);
         }
-        // online softmax over the quarter's keys 16w + 8h + 0..7 of this lane's pair
+        // online softmax over the quarter's keys 16 qw + 8h + 0..7 of this lane's pair
         if (!is_full(tile)) {
-            const int kb = tile * BN + 16 * wave + 8 * h;
+            const int kb = tile * BN + 16 * qw + 8 * h;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (kb + j < lo || kb + j > last) x[j] = -INFINITY;
@@ -360,91 +391,92 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
                 if (NP == 3) plo.w[u] = cvt_pk_bf16(e0 - lo_bf16(pmid.w[u]), e1 - hi_bf16(pmid.w[u]));
             }
         }
+        {
+            const __amdgpu_buffer_rsrc_t nrk = qdesc(kg, nso, nfast);
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-            Pack8 av;
-            av.w[0] = vx[db][0].x;
-            av.w[1] = vx[db][0].y;
-            av.w[2] = vx[db][1].x;
-            av.w[3] = vx[db][1].y;
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
-            if (NP >= 2) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
-            if (NP == 3) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
-            buffer_to_lds16(nrv, nvd + 1024 * db, lane_off[db]);   // next quarter's V
-        }
-        // keep that order: per 32-dim block its NP products, then one load of the next quarter
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NP, 1);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-        }
-    };
-
-    // one tile of this wave (no barrier: a wave reads only the rows it loaded itself): the
-    // quarter loads the next quarter on the fast path itself; an edge next quarter (the ends
-    // of the range, a ring wrap), or the next quarter of a tile this wave skips, is issued
-    // whole afterwards
-    //
-    // ns, nso: ring slot and element offset of this wave's quarter of the tile after the
-    // current one, advanced a tile at a time (one wrap per tile in a ring of at least 64
-    // slots, a loop in a shorter one) instead of a remainder and a product per tile
-    int ns = ring_slot(a, (t0 + 1) * BN + 16 * wave);
-    int64_t nso = (int64_t)ns * a.kv_sslot;
-    const int64_t tile_elems = (int64_t)BN * a.kv_sslot, ring_elems = (int64_t)a.ring * a.kv_sslot;
-    auto step = [&](int tile, const char* kt, const char* vt, char* knext, char* vnext, bool more) {
-        const bool nxt = more && meets(tile + 1);
-        const bool fast = nxt && prep_at(tile + 1, ns, nso, knext, vnext, kmax).fast;
-        const bool here = meets(tile);
-        if (here) quarter(fast, nso, tile, kt, vt, knext, vnext);
-        if (nxt && !(here && fast)) issue_all(prep_at(tile + 1, ns, nso, knext, vnext, kmax));
-        ns += BN;
-        nso += tile_elems;
-        while (ns >= a.ring) {
-            ns -= a.ring;
-            nso -= ring_elems;
-        }
-    };
-
-    if (a.scale < 0.f) {
-        // a negative scale is carried by q's sign (exact), so the exponent factor is positive
-        // (a branch, so that a positive scale does not wait for the q loads here)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qreg[nb][ks].u.x ^= 0x80008000u; qreg[nb][ks].u.y ^= 0x80008000u;
-                qreg[nb][ks].u.z ^= 0x80008000u; qreg[nb][ks].u.w ^= 0x80008000u;
+            for (int db = 0; db < DBLK; ++db) {
+                Pack8 av;
+                av.w[0] = vx[db][0].x;
+                av.w[1] = vx[db][0].y;
+                av.w[2] = vx[db][1].x;
+                av.w[3] = vx[db][1].y;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, phi.v, oacc[db], 0, 0, 0);
+                if (NP >= 2) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, pmid.v, oacc[db], 0, 0, 0);
+                if (NP == 3) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
+                lds_dma_buffer16(nrk, lane_off[db], mk + 1024 * db);
             }
-    }
-    for (int t = t0; t <= t1; t += 2) {
-        step(t, Ks0, Vs0, Ks1, Vs1, t + 1 <= t1);
-        if (t + 1 <= t1) step(t + 1, Ks1, Vs1, Ks0, Vs0, t + 2 <= t1);
-    }
-    // merge of the four quarters' states. A wave's own rows of the four stage arrays (rows
-    // 16w .. 16w + 15 of every tile, 8 KiB in each) are touched by no other wave and hold
-    // exactly its O: once its own loads have landed it stores O there without waiting for
-    // the other waves, dims 64j .. 64j + 63 into array j (pair-major, 256 bytes a pair, the
-    // 16-byte chunk c of pair p at c ^ (p & 15)), and (m, l) into red_*.
-    const float l_tot = pair_sum(l_run);
-    char* const arrs[kWaves] = {Ks0, Vs0, Ks1, Vs1};
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = 32 * db + 8 * q4 + 4 * h;        // dims d0 .. d0 + 3
-            const int c = (d0 & 63) >> 2;                   // chunk within the 64-dim block
-            float* ob = reinterpret_cast<float*>(arrs[d0 >> 6] + 16 * RB * wave) + col * 64;
-            *reinterpret_cast<float4*>(ob + 4 * (c ^ (col & 15))) =
-                make_float4(oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]);
+            if (more && !nfast) issue_edge(kg, tile + 2, mk);
         }
-    if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
-    lds_barrier();
-    // wave w produces dims 64w + 32h + 0..31 of pair col from array w; a (row, head) with a
-    // non-finite value is flagged before any of its values is stored, and re-run below instead
-    const char* const mine = wave == 0 ? Ks0 : wave == 1 ? Vs0 : wave == 2 ? Ks1 : Vs1;
+        if (!more) break;
+        cs = ns;
+        cso = nso;
+    }
+
+    // Merge of the eight states. Phase 1: the odd-tile wave of each quarter stores its O (pair
+    // col's dims in 1 KiB, 16-byte chunk c at c ^ (col & 15)) into array qw of the four stage
+    // arrays and its (m, l) into red_*, and the even-tile wave folds it into its own state.
+    const float l_tot = pair_sum(l_run);
+    auto arrs = [&](int j) __attribute__((always_inline)) {
+        return j == 0 ? Ks[0] : j == 1 ? Vs[0] : j == 2 ? Ks[1] : Vs[1];
+    };
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();                       // every wave is done with the stages
+    auto o_chunk = [&](char* base, int db, int k) __attribute__((always_inline)) {
+        const int c = (32 * db + 8 * k + 4 * h) >> 2;    // dims 4c .. 4c + 3
+        return reinterpret_cast<float4*>(base + col * 1024 + 16 * ((c & ~15) | ((c & 15) ^ (col & 15))));
+    };
+    if (par == 1) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *o_chunk(arrs(qw), db, k) = make_float4(oacc[db][4 * k], oacc[db][4 * k + 1], oacc[db][4 * k + 2], oacc[db][4 * k + 3]);
+        if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
+    }
+    __syncthreads();
+    float m_pair = m_run, l_pair = l_tot;
+    if (par == 0) {
+        const float m1 = red_m[wave + 4][col], l1 = red_l[wave + 4][col];
+        const float M2 = fmaxf(m_run, m1);
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M2);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M2);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 o1 = *o_chunk(arrs(qw), db, k);
+                oacc[db][4 * k] = fmaf(a1, o1.x, a0 * oacc[db][4 * k]);
+                oacc[db][4 * k + 1] = fmaf(a1, o1.y, a0 * oacc[db][4 * k + 1]);
+                oacc[db][4 * k + 2] = fmaf(a1, o1.z, a0 * oacc[db][4 * k + 2]);
+                oacc[db][4 * k + 3] = fmaf(a1, o1.w, a0 * oacc[db][4 * k + 3]);
+            }
+        m_pair = M2;
+        l_pair = fmaf(a1, l1, a0 * l_tot);
+    }
+    __syncthreads();
+    // Phase 2, the even-tile waves: wave qw stores its O into its own rows of the four arrays
+    // (rows 16 qw .. + 15, 8 KiB in each), dims 64j .. 64j + 63 into array j (pair-major, 256
+    // bytes a pair, the 16-byte chunk c of pair p at c ^ (p & 15)), and (m, l) into red_*.
+    if (par == 0) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int d0 = 32 * db + 8 * k + 4 * h;          // dims d0 .. d0 + 3
+                const int c = (d0 & 63) >> 2;                   // chunk within the 64-dim block
+                float* ob = reinterpret_cast<float*>(arrs(d0 >> 6) + 16 * RB * qw) + col * 64;
+                *reinterpret_cast<float4*>(ob + 4 * (c ^ (col & 15))) =
+                    make_float4(oacc[db][4 * k], oacc[db][4 * k + 1], oacc[db][4 * k + 2], oacc[db][4 * k + 3]);
+            }
+        if (h == 0) { red_m[qw][col] = m_pair; red_l[qw][col] = l_pair; }
+    }
+    __syncthreads();
+    // even-tile wave w produces dims 64w + 32h + 0..31 of pair col from array w; a (row, head)
+    // with a non-finite value is flagged before any of its values is stored, and re-run below
+    // instead
     uint2 res[8];
-    if (valid) {
+    if (par == 0 && valid) {
+        const char* const mine = arrs(qw);
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][col]);
@@ -463,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         uint32_t expo = 0;                 // OR of the exponent fields: all ones = not finite
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = 8 * h + i;                         // dims 64 wave + 4c .. + 3
+            const int c = 8 * h + i;                         // dims 64 qw + 4c .. + 3
             float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
@@ -482,9 +514,9 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_quarter_kernel(PromptArgs 
         }
         if (expo) bad[col] = 1;
     }
-    lds_barrier();
-    if (valid && !bad[col]) {
-        uint16_t* op = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead + 64 * wave + 32 * h;
+    __syncthreads();
+    if (par == 0 && valid && !bad[col]) {
+        uint16_t* op = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead + 64 * qw + 32 * h;
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(op + 4 * i) = res[i];
     }
@@ -509,7 +541,7 @@ template <int NP>
 hipError_t launch_quarter(const PromptArgs& b, hipStream_t s) {
     const int G = b.hq / b.hkv;
     const int nblk = (int)(((int64_t)b.n * G + kQuarterPairs - 1) / kQuarterPairs);
-    hipLaunchKernelGGL((prompt_quarter_kernel<NP>), dim3((unsigned)(nblk * b.hkv)), dim3(kThreads), 0, s, b, nblk);
+    hipLaunchKernelGGL((prompt_quarter_kernel<NP>), dim3((unsigned)(nblk * b.hkv)), dim3(kOctThreads), 0, s, b, nblk);
     return hipGetLastError();
 }
 

@@ -46,26 +46,6 @@ namespace {
 
 constexpr int kRowCols = 16;           // (row, head) columns per workgroup
 
-// LDS loads issued as inline assembly (they write LDS only, no register): the compiler does not
-// track them, so each wait on them is written out (lds_dma_wait_vm16, s_waitcnt before the
-// results are read). M0 holds the wave's LDS destination; lane i's 16 bytes land at M0 + 16 i.
-// Volatile statements keep their order among themselves; the waits below also order every
-// memory access around them, so an LDS read and the load that refills its stage stay on either
-// side of a wait.
-__device__ __forceinline__ void lds_dma_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(m0), "s"(rsrc));
-}
-__device__ __forceinline__ void lds_dma_global16(const void* src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(m0));
-}
-// all but the last 16 vector-memory loads have landed; all have
-__device__ __forceinline__ void lds_dma_wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
-__device__ __forceinline__ void lds_dma_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// every LDS read issued so far has returned
-__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ int ctz64(uint64_t x) { return __builtin_ctzll(x); }
 
 template <int NP>
@@ -181,10 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void prompt_rows_kernel(PromptArgs a, 
         return __builtin_amdgcn_make_buffer_rsrc((void*)(src + (int64_t)sq * a.kv_sslot), (short)0,
                                                  use ? quarter_extent : 0, 0x00020000);
     };
-    auto lds_base = [&](const char* dst) __attribute__((always_inline)) {
-        return (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)(uint32_t)(uintptr_t)(lds_void_ptr)(dst + 16 * RB * wave));
-    };
+    auto lds_base = [&](const char* dst) __attribute__((always_inline)) { return lds_addr(dst + 16 * RB * wave); };
     // a quarter key by key: key qb + r clamped into [kmin, kmax] and wrapped into the ring,
     // counted from the quarter's first key clamped into that range (every clamped key lies
     // 0 .. 15 keys after it: one wrap at most in a ring of at least 16 slots; a selected block

@@ -47,8 +47,10 @@ __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t*
     __shared__ double qs[D];
     __shared__ double ps[D];
     __shared__ double red[D];
+    // threads D .. blockDim - 1 (a workgroup wider than D) take part in the barriers only
     const int t = threadIdx.x;
-    qs[t] = (double)bf16_to_f32(q[t]);
+    const bool act = t < D;
+    if (act) qs[t] = (double)bf16_to_f32(q[t]);
     __syncthreads();
     const double c = (double)scale;
     auto score = [&](int j) {
@@ -59,9 +61,10 @@ __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t*
     };
     // pass 1: the maximum score (a NaN score reaches the output through its weight)
     double mx = -INFINITY;
-    for (int j = lo + t; j <= last; j += D)
-        if (sel(j)) mx = fmax(mx, score(j));
-    red[t] = mx;
+    if (act)
+        for (int j = lo + t; j <= last; j += D)
+            if (sel(j)) mx = fmax(mx, score(j));
+    if (act) red[t] = mx;
     __syncthreads();
     for (int w = D / 2; w > 0; w >>= 1) {
         if (t < w) red[t] = fmax(red[t], red[t + w]);
@@ -74,25 +77,25 @@ __device__ void rerun_f64(const uint16_t* q, const uint16_t* kb, const uint16_t*
     for (int base = lo; base <= last; base += D) {
         const int j = base + t;
         double p = 0.0;
-        if (j <= last && sel(j)) p = exp(score(j) - m);
-        ps[t] = p;
+        if (act && j <= last && sel(j)) p = exp(score(j) - m);
+        if (act) ps[t] = p;
         l += p;
         __syncthreads();
-        const int nk = min(D, last - base + 1);
+        const int nk = act ? min(D, last - base + 1) : 0;
         for (int i = 0; i < nk; ++i) {
             const int jj = base + i;
             if (sel(jj)) x += ps[i] * (double)bf16_to_f32(vb[(int64_t)(jj % ring) * sslot + t]);
         }
         __syncthreads();
     }
-    red[t] = l;
+    if (act) red[t] = l;
     __syncthreads();
     for (int w = D / 2; w > 0; w >>= 1) {
         if (t < w) red[t] = red[t] + red[t + w];
         __syncthreads();
     }
     const double lsum = 0.0 + red[0];
-    out[t] = (uint16_t)f64_to_bf16_rne((0.0 + x) / lsum);
+    if (act) out[t] = (uint16_t)f64_to_bf16_rne((0.0 + x) / lsum);
 }
 
 }  // namespace wa
