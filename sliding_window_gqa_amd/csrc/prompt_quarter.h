@@ -11,10 +11,9 @@
 // (absolute index) of the block's key range (w < 4) or of the odd ones (w >= 4), with a
 // running (m, l, O) of its
 // own; the two waves of a SIMD work on different tiles, so one's softmax runs while the
-// other's matrix products do. After the last tile the eight states are merged in LDS: each
-// odd-tile wave into the even-tile wave of the same quarter, then the four in quarter order
-// (M = max m_w, a_w = 2^(m_w - M), den = sum a_w l_w, out = bf16(sum (a_w / den) O_w), the
-// sums fma chains in w order). So every row is finished inside its workgroup: no fp32
+// other's matrix products do. After the last tile the eight states are merged in LDS, in
+// wave order (M = max m_w, a_w = 2^(m_w - M), den = sum a_w l_w, out = bf16(sum (a_w / den)
+// O_w), the sums fma chains in w order), half of the dims at a time. So every row is finished inside its workgroup: no fp32
 // partials leave the CU and no merge kernel follows; a (row, head) whose bf16 output is not
 // finite is re-run in float64 by the same workgroup (rerun_f64.h), so no check kernel
 // follows either. A row's bits depend only on its key range and the absolute tile grid (a
@@ -137,15 +136,10 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
     const int row_first = blk * kQuarterPairs / G;
     if (row_first >= a.n) return;          // no valid pair in this workgroup (uniform)
     const int kmin = prompt_lo(a, row_first);
-    const int big = 0x7FFFFFFF;
-    int lo = big, last = -1;               // empty range for padding pairs
-    if (valid) prompt_span(a, row, lo, last);
-    // every wave holds the same 32 pairs, so these are the workgroup's values as well; kept in
-    // scalar registers so that the tile addresses and descriptors derived from them are too
-    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(last));
-    const int loall = __builtin_amdgcn_readfirstlane(wave_max_i(valid ? lo : -1));
-    const int lastall = __builtin_amdgcn_readfirstlane(wave_min_i(valid ? last : big));
-    const int t0 = kmin / BN, t1 = kmax / BN;
+    // every valid row's last key is at least its own position, so the last valid row's
+    // position is a lower bound of the block's last key kmax (known before hi is)
+    const int kmax_low = a.p0 + min(a.n - 1, (blk * kQuarterPairs + kQuarterPairs - 1) / G);
+    const int t0 = kmin / BN;
 
     const uint16_t* kg = a.k + (int64_t)g * a.kv_shead;
     const uint16_t* vg = a.v + (int64_t)g * a.kv_shead;
@@ -168,40 +162,72 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
     char* const vst = Vs[par] + 16 * RB * qw;
     const uint32_t mk = lds_addr(kst), mv = lds_addr(vst);
     // quarter of tile `tile` whose first key sits in ring slot sq (element offset so)
-    auto is_fast = [&](int tile, int sq) __attribute__((always_inline)) {
+    auto is_fast = [&](int tile, int sq, int kcap) __attribute__((always_inline)) {
         const int qb = tile * BN + 16 * qw;
-        return qb >= kmin && qb + 15 <= kmax && sq + 16 <= a.ring;
+        return qb >= kmin && qb + 15 <= kcap && sq + 16 <= a.ring;
     };
     auto qdesc = [&](const uint16_t* src, int64_t so, bool use) __attribute__((always_inline)) {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(src + so), (short)0, use ? quarter_extent : 0, 0x00020000);
     };
-    // key qb + r clamped into [kmin, kmax] and wrapped into the ring, counted from the
+    // key qb + r clamped into [kmin, kcap] and wrapped into the ring, counted from the
     // quarter's first key clamped into that range (every clamped key lies 0 .. 15 keys after
     // it: one wrap at most in a ring of at least 16 slots)
-    auto issue_edge = [&](const uint16_t* src, int tile, uint32_t m0) __attribute__((always_inline)) {
+    auto issue_edge = [&](const uint16_t* src, int tile, uint32_t m0, int kcap) __attribute__((always_inline)) {
         const int qb = tile * BN + 16 * qw;
-        const int qbc = min(max(qb, kmin), kmax);
+        const int qbc = min(max(qb, kmin), kcap);
         const int sqc = ring_slot(a, qbc);
 #pragma unroll
         for (int i = 0; i < QL; ++i) {
             const int r = RPK * i + ld_row;
             const int c = (ld_p & ~15) | ((ld_p & 15) ^ swz(r));
-            const int jc = min(max(qb + r, kmin), kmax);
+            const int jc = min(max(qb + r, kmin), kcap);
             int slot = sqc + (jc - qbc);
             if (a.ring >= 16) slot = slot >= a.ring ? slot - a.ring : slot;
             else slot = jc % a.ring;
             lds_dma_global16(src + (int64_t)slot * a.kv_sslot + 8 * c, m0 + 1024 * i);
         }
     };
-    auto issue_whole = [&](const uint16_t* src, int tile, int sq, int64_t so, uint32_t m0) __attribute__((always_inline)) {
-        if (is_fast(tile, sq)) {
+    auto issue_whole = [&](const uint16_t* src, int tile, int sq, int64_t so, uint32_t m0, int kcap) __attribute__((always_inline)) {
+        if (is_fast(tile, sq, kcap)) {
             const __amdgpu_buffer_rsrc_t rs = qdesc(src, so, true);
 #pragma unroll
             for (int i = 0; i < QL; ++i) lds_dma_buffer16(rs, lane_off[i], m0 + 1024 * i);
         } else {
-            issue_edge(src, tile, m0);
+            issue_edge(src, tile, m0, kcap);
         }
     };
+
+    // This wave's first quarter goes out before hi is known when it lies wholly below kmax_low
+    // (so no key of it is clamped at the top, and kmax >= kmax_low means it meets the range);
+    // hi's latency, the tile's and q's then overlap.
+    const int ta0 = t0 + ((par - t0) & 1);
+    const int qb0 = ta0 * BN + 16 * qw;
+    const bool early = qb0 + 15 >= kmin && qb0 + 15 <= kmax_low;
+    if (early) {
+        const int sq0 = ring_slot(a, qb0);
+        issue_whole(vg, ta0, sq0, (int64_t)sq0 * a.kv_sslot, mv, kmax_low);
+        issue_whole(kg, ta0, sq0, (int64_t)sq0 * a.kv_sslot, mk, kmax_low);
+    }
+    // the block's q, requested now (stored into LDS before the walk)
+    uint4 qv[kQuarterPairs * CPR / kOctThreads];
+#pragma unroll
+    for (int k = 0; k < kQuarterPairs * CPR / kOctThreads; ++k) {
+        const int i = tid + kOctThreads * k;
+        const int p = i / CPR, c = i % CPR;
+        const int pr = blk * kQuarterPairs + p;
+        const int qrow = pr / G;
+        qv[k] = *reinterpret_cast<const uint4*>(
+            a.q + (int64_t)(qrow < a.n ? qrow : 0) * a.q_srow + (int64_t)(g * G + pr % G) * a.q_shead + 8 * c);
+    }
+    const int big = 0x7FFFFFFF;
+    int lo = big, last = -1;               // empty range for padding pairs
+    if (valid) prompt_span(a, row, lo, last);
+    // every wave holds the same 32 pairs, so these are the workgroup's values as well; kept in
+    // scalar registers so that the tile addresses and descriptors derived from them are too
+    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(last));
+    const int loall = __builtin_amdgcn_readfirstlane(wave_max_i(valid ? lo : -1));
+    const int lastall = __builtin_amdgcn_readfirstlane(wave_min_i(valid ? last : big));
+    const int t1 = kmax / BN;
 
     // this wave's tiles: those of its parity (absolute tile index, so that a row's bits do not
     // depend on where a call's first block starts) that its quarter meets (keys of the
@@ -214,7 +240,7 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
         const int qb = tile * BN + 16 * qw;
         return qb >= loall && qb + 15 <= lastall;
     };
-    int ta = t0 + ((par - t0) & 1);
+    int ta = ta0;
     if (ta <= t1 && !meets(ta)) ta += 2;
     int tz = t1 - ((t1 - par) & 1);                    // last tile of this parity
     if (tz >= ta && !meets(tz)) tz -= 2;
@@ -232,9 +258,9 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
             so -= ring_elems;
         }
     };
-    if (work) {                            // the first quarter: V, then K
-        issue_whole(vg, ta, cs, cso, mv);
-        issue_whole(kg, ta, cs, cso, mk);
+    if (work && !(early && ta == ta0)) {  // the first quarter, if not out already: V, then K
+        issue_whole(vg, ta, cs, cso, mv, kmax);
+        issue_whole(kg, ta, cs, cso, mk, kmax);
     }
 
     // the block's q into LDS (a padding pair takes row 0's q: its range is empty, so every key
@@ -246,12 +272,8 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
         for (int k = 0; k < kQuarterPairs * CPR / kOctThreads; ++k) {
             const int i = tid + kOctThreads * k;
             const int p = i / CPR, c = i % CPR;
-            const int pr = blk * kQuarterPairs + p;
-            const int qrow = pr / G;
-            const uint4 v = *reinterpret_cast<const uint4*>(
-                a.q + (int64_t)(qrow < a.n ? qrow : 0) * a.q_srow + (int64_t)(g * G + pr % G) * a.q_shead + 8 * c);
             *reinterpret_cast<uint4*>(Qs + p * RB + 16 * ((c & ~15) | ((c & 15) ^ (p & 15)))) =
-                make_uint4(v.x ^ sgn, v.y ^ sgn, v.z ^ sgn, v.w ^ sgn);
+                make_uint4(qv[k].x ^ sgn, qv[k].y ^ sgn, qv[k].z ^ sgn, qv[k].w ^ sgn);
         }
     }
     __syncthreads();
@@ -301,7 +323,7 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
         int ns = cs;
         int64_t nso = cso;
         advance(ns, nso);
-        const bool nfast = more && is_fast(tile + 2, ns);
+        const bool nfast = more && is_fast(tile + 2, ns, kmax);
 
         lds_dma_wait_vm8();                // this quarter's V (its K may still be in flight)
         uint2 vx[DBLK][2];
@@ -332,7 +354,7 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
                 s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf.v, qb.v, s[1], 0, 0, 0);
                 lds_dma_buffer16(nrv, lane_off[ks], mv + 1024 * ks);
             }
-            if (more && !nfast) issue_edge(vg, tile + 2, mv);
+            if (more && !nfast) issue_edge(vg, tile + 2, mv, kmax);
         }
         lds_wait_reads();                  // K read: the stage may be refilled
         // to the P^T layout: lane l = 32a + 16b + c holds pair 16b + c; its keys 8a + i come
@@ -405,120 +427,92 @@ __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptAr
                 if (NP == 3) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
                 lds_dma_buffer16(nrk, lane_off[db], mk + 1024 * db);
             }
-            if (more && !nfast) issue_edge(kg, tile + 2, mk);
+            if (more && !nfast) issue_edge(kg, tile + 2, mk, kmax);
         }
         if (!more) break;
         cs = ns;
         cso = nso;
     }
 
-    // Merge of the eight states. Phase 1: the odd-tile wave of each quarter stores its O (pair
-    // col's dims in 1 KiB, 16-byte chunk c at c ^ (col & 15)) into array qw of the four stage
-    // arrays and its (m, l) into red_*, and the even-tile wave folds it into its own state.
+    // Merge of the eight states, in two halves of the dims (the eight O would not fit in LDS
+    // at once). For half hh every wave stores its O of dims 128 hh .. + 127 (32 pairs x 512
+    // bytes, 16-byte chunk c of pair col at c ^ (col & 15)) into the half of stage array w % 4
+    // numbered w / 4, and its (m, l) into red_*; then wave w produces dims 128 hh + 16 w ..
+    // + 15 of every pair: M = max m_v, a_v = 2^(m_v - M), den = sum a_v l_v, out =
+    // bf16(sum (a_v / den) O_v), the sums fma chains in wave order. A (row, head) with a
+    // non-finite value is flagged, not stored, and re-run below.
     const float l_tot = pair_sum(l_run);
     auto arrs = [&](int j) __attribute__((always_inline)) {
         return j == 0 ? Ks[0] : j == 1 ? Vs[0] : j == 2 ? Ks[1] : Vs[1];
     };
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();                       // every wave is done with the stages
-    auto o_chunk = [&](char* base, int db, int k) __attribute__((always_inline)) {
-        const int c = (32 * db + 8 * k + 4 * h) >> 2;    // dims 4c .. 4c + 3
-        return reinterpret_cast<float4*>(base + col * 1024 + 16 * ((c & ~15) | ((c & 15) ^ (col & 15))));
+    auto region = [&](int w) __attribute__((always_inline)) { return arrs(w & 3) + (TILE_B / 2) * (w >> 2); };
+    auto o_chunk = [&](const char* base, int c) __attribute__((always_inline)) {
+        return reinterpret_cast<const float4*>(base + col * 512 + 16 * ((c & ~15) | ((c & 15) ^ (col & 15))));
     };
-    if (par == 1) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                *o_chunk(arrs(qw), db, k) = make_float4(oacc[db][4 * k], oacc[db][4 * k + 1], oacc[db][4 * k + 2], oacc[db][4 * k + 3]);
-        if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
-    }
-    __syncthreads();
-    float m_pair = m_run, l_pair = l_tot;
-    if (par == 0) {
-        const float m1 = red_m[wave + 4][col], l1 = red_l[wave + 4][col];
-        const float M2 = fmaxf(m_run, m1);
-        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M2);
-        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M2);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 o1 = *o_chunk(arrs(qw), db, k);
-                oacc[db][4 * k] = fmaf(a1, o1.x, a0 * oacc[db][4 * k]);
-                oacc[db][4 * k + 1] = fmaf(a1, o1.y, a0 * oacc[db][4 * k + 1]);
-                oacc[db][4 * k + 2] = fmaf(a1, o1.z, a0 * oacc[db][4 * k + 2]);
-                oacc[db][4 * k + 3] = fmaf(a1, o1.w, a0 * oacc[db][4 * k + 3]);
-            }
-        m_pair = M2;
-        l_pair = fmaf(a1, l1, a0 * l_tot);
-    }
-    __syncthreads();
-    // Phase 2, the even-tile waves: wave qw stores its O into its own rows of the four arrays
-    // (rows 16 qw .. + 15, 8 KiB in each), dims 64j .. 64j + 63 into array j (pair-major, 256
-    // bytes a pair, the 16-byte chunk c of pair p at c ^ (p & 15)), and (m, l) into red_*.
-    if (par == 0) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int d0 = 32 * db + 8 * k + 4 * h;          // dims d0 .. d0 + 3
-                const int c = (d0 & 63) >> 2;                   // chunk within the 64-dim block
-                float* ob = reinterpret_cast<float*>(arrs(d0 >> 6) + 16 * RB * qw) + col * 64;
-                *reinterpret_cast<float4*>(ob + 4 * (c ^ (col & 15))) =
-                    make_float4(oacc[db][4 * k], oacc[db][4 * k + 1], oacc[db][4 * k + 2], oacc[db][4 * k + 3]);
-            }
-        if (h == 0) { red_m[qw][col] = m_pair; red_l[qw][col] = l_pair; }
-    }
-    __syncthreads();
-    // even-tile wave w produces dims 64w + 32h + 0..31 of pair col from array w; a (row, head)
-    // with a non-finite value is flagged before any of its values is stored, and re-run below
-    // instead
-    uint2 res[8];
-    if (par == 0 && valid) {
-        const char* const mine = arrs(qw);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (h == 0) { red_m[wave][col] = m_run; red_l[wave][col] = l_tot; }
+    __syncthreads();                       // every wave is done with the stages
+    float ac[kOctWaves];
+    {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][col]);
-        float ac[kWaves], den = 0.f;
+        for (int w = 0; w < kOctWaves; ++w) M = fmaxf(M, red_m[w][col]);
+        float den = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kOctWaves; ++w) {
             const float mw = red_m[w][col];
             ac[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             den = fmaf(ac[w], red_l[w][col], den);
         }
-        // out = sum_w (a_w / den) O_w: one division a lane instead of one per value (den = 0,
-        // a row without keys, gives NaN and a float64 re-run, as 0 / 0 would)
+        // one division a lane instead of one per value (den = 0, a row without keys, gives
+        // NaN and a float64 re-run, as 0 / 0 would)
         const float rden = 1.f / den;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) ac[w] *= rden;
-        uint32_t expo = 0;                 // OR of the exponent fields: all ones = not finite
+        for (int w = 0; w < kOctWaves; ++w) ac[w] *= rden;
+    }
+    uint2 res[2][2];
+    uint32_t expo = 0;                     // OR of the exponent fields: all ones = not finite
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = 8 * h + i;                         // dims 64 qw + 4c .. + 3
+    for (int hh = 0; hh < 2; ++hh) {
+        // O^T layout: register 4k + i of block db holds dims 32 db + 8k + 4h + i
+        char* const mine = region(wave);
+#pragma unroll
+        for (int db = 4 * hh; db < 4 * hh + 4; ++db)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = ((32 * db + 8 * k + 4 * h) & 127) >> 2;
+                *reinterpret_cast<float4*>(mine + col * 512 + 16 * ((c & ~15) | ((c & 15) ^ (col & 15)))) =
+                    make_float4(oacc[db][4 * k], oacc[db][4 * k + 1], oacc[db][4 * k + 2], oacc[db][4 * k + 3]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = 4 * wave + 2 * h + i;              // dims 128 hh + 4c .. + 3
             float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float4 o = *reinterpret_cast<const float4*>(
-                    reinterpret_cast<const float*>(mine + 16 * RB * w) + col * 64 + 4 * (c ^ (col & 15)));
+            for (int w = 0; w < kOctWaves; ++w) {
+                const float4 o = *o_chunk(region(w), c);
                 num.x = fmaf(ac[w], o.x, num.x);
                 num.y = fmaf(ac[w], o.y, num.y);
                 num.z = fmaf(ac[w], o.z, num.z);
                 num.w = fmaf(ac[w], o.w, num.w);
             }
-            res[i].x = cvt_pk_bf16(num.x, num.y);
-            res[i].y = cvt_pk_bf16(num.z, num.w);
-            const uint32_t e0 = res[i].x & 0x7F807F80u, e1 = res[i].y & 0x7F807F80u;
+            res[hh][i].x = cvt_pk_bf16(num.x, num.y);
+            res[hh][i].y = cvt_pk_bf16(num.z, num.w);
+            const uint32_t e0 = res[hh][i].x & 0x7F807F80u, e1 = res[hh][i].y & 0x7F807F80u;
             expo |= ((e0 & 0x7F80u) == 0x7F80u) | ((e0 >> 16) == 0x7F80u) |
                     ((e1 & 0x7F80u) == 0x7F80u) | ((e1 >> 16) == 0x7F80u);
         }
-        if (expo) bad[col] = 1;
+        __syncthreads();                   // the regions are read before the next half's stores
     }
+    if (valid && expo) bad[col] = 1;
     __syncthreads();
-    if (par == 0 && valid && !bad[col]) {
-        uint16_t* op = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead + 64 * qw + 32 * h;
+    if (valid && !bad[col]) {
+        uint16_t* op = a.out + (int64_t)row * a.o_srow + (int64_t)head * a.o_shead + 16 * wave + 8 * h;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(op + 4 * i) = res[i];
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) *reinterpret_cast<uint2*>(op + 128 * hh + 4 * i) = res[hh][i];
     }
     // a (row, head) whose output holds a NaN or an infinity is re-run alone in float64 by the
     // whole workgroup; the flag is read from LDS by every thread, so the branch is uniform
