@@ -643,8 +643,8 @@ def main():
                              "flop_accounting": "(2 + 2*3) * d per selected visible (row, head, key)"}
     res["roofline_prefill_sparse"] = roofline(
         "mfma", stf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
-        traffic_bytes("sparse", ["prompt_kernel", "prompt_merge_kernel"]),
-        "prompt_kernel<256,3 parts> sparse + prompt_merge_kernel")
+        traffic_bytes("sparse", ["prompt_rows_kernel", "prompt_merge_kernel"]),
+        "prompt_rows_kernel<3 parts> + prompt_merge_kernel (sparse slice)")
 
     if not args.no_long and not args.no_prep:
         pr = Preparer()
