@@ -10,9 +10,6 @@ namespace wa {
 hipError_t launch_prompt_main_128_1(const PromptArgs&, int, unsigned, hipStream_t);
 hipError_t launch_prompt_main_128_2(const PromptArgs&, int, unsigned, hipStream_t);
 hipError_t launch_prompt_main_128_3(const PromptArgs&, int, unsigned, hipStream_t);
-hipError_t launch_prompt_main_256_1(const PromptArgs&, int, unsigned, hipStream_t);
-hipError_t launch_prompt_main_256_2(const PromptArgs&, int, unsigned, hipStream_t);
-hipError_t launch_prompt_main_256_3(const PromptArgs&, int, unsigned, hipStream_t);
 hipError_t launch_prompt_quarter_1(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_quarter_2(const PromptArgs&, hipStream_t);
 hipError_t launch_prompt_quarter_3(const PromptArgs&, hipStream_t);
@@ -45,22 +42,16 @@ hipError_t launch_prompt(const PromptArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         return launch_prompt_post_256(b, s);
     }
+    // d = 128: the 128-pair kernel, then the merge of a split prompt's chunk partials (or the
+    // check of an unsplit one)
     const int G = a.hq / a.hkv;
     const int nblk = (int)(((int64_t)a.n * G + kPromptPairs - 1) / kPromptPairs);
     const unsigned grid = (unsigned)(nblk * a.hkv * a.nchunk);
-    const PromptArgs& b = a;
-    hipError_t e;
-    if (D == 256) {
-        e = a.p_parts == 3 ? launch_prompt_main_256_3(b, nblk, grid, s)
-          : a.p_parts == 2 ? launch_prompt_main_256_2(b, nblk, grid, s)
-                           : launch_prompt_main_256_1(b, nblk, grid, s);
-    } else {
-        e = a.p_parts == 3 ? launch_prompt_main_128_3(b, nblk, grid, s)
-          : a.p_parts == 2 ? launch_prompt_main_128_2(b, nblk, grid, s)
-                           : launch_prompt_main_128_1(b, nblk, grid, s);
-    }
+    const hipError_t e = a.p_parts == 3 ? launch_prompt_main_128_3(a, nblk, grid, s)
+                       : a.p_parts == 2 ? launch_prompt_main_128_2(a, nblk, grid, s)
+                                        : launch_prompt_main_128_1(a, nblk, grid, s);
     if (e != hipSuccess) return e;
-    return D == 256 ? launch_prompt_post_256(a, s) : launch_prompt_post_128(a, s);
+    return launch_prompt_post_128(a, s);
 }
 
 }  // namespace wa

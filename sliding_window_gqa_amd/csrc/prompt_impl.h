@@ -38,11 +38,9 @@
 //   * the workgroup index is remapped so that each XCD (8 on MI355X, workgroups dealt out
 //     round-robin) works through a contiguous range of (key head, row block) tiles, keeping
 //     a key head's K/V stream in that XCD's L2;
-//   * at d = 256 (one wave a SIMD) the MFMA accumulators stay in VGPRs (the library is built
-//     with -amdgpu-mfma-vgpr-form), the V^T fragments of the next 16-key step are read while
-//     the current step's MFMAs run, and the Q loads stay in flight across the set-up.
-// This kernel serves prompts at d = 128 and block-sparse prompts at d = 256; dense prompts at
-// d = 256 take the quarter-tile kernel (prompt_quarter.h).
+// This kernel serves prompts at d = 128 (dense, windowed or not, and block-sparse); prompts at
+// d = 256 take the quarter-tile kernel (prompt_quarter.h, dense) or the row-group kernel
+// (prompt_sparse.h, block-sparse).
 //
 // This header holds the kernels; prompt_inst.hip instantiates them once per (head dim, parts
 // of P), so that they compile in parallel, and prompt.hip holds the launcher.
@@ -154,7 +152,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D, int NP>
-__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(PromptArgs a, int nblk) {
+__global__ __launch_bounds__(kThreads, 2) void prompt_kernel(PromptArgs a, int nblk) {
+    static_assert(D == 128, "prompts at d = 256 take prompt_quarter.h (dense) or prompt_sparse.h (block-sparse)");
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
     constexpr int RB = 2 * D;              // bytes per K/V row in LDS
@@ -195,35 +194,28 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     const int head = g * G + pair % G;
     const bool valid = row < a.n;
 
-    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7. At d = 128 (long prompts, where
-    // the set-up below is a negligible part) it is loaded first and waited for at the first
-    // barrier. At d = 256 it is loaded once the row's last key is known, and its loads stay in
-    // flight over the key-range set-up and the first tile loads (the barriers before its
-    // first use wait for LDS operations only); a padding pair then takes row 0's q (each
-    // pair is its own MFMA column and a padding pair's output is never written).
+    // Q^T operand: this lane's pair, dims 16*ks + 8*h + 0..7, loaded first and waited for at
+    // the first barrier (zeros for a padding pair)
     Pack8 qreg[KSTEPS];
-    auto load_q = [&]() __attribute__((always_inline)) {
-        const uint16_t* qp = a.q + (int64_t)(D == 256 && !valid ? 0 : row) * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
+    {
+        const uint16_t* qp = a.q + (int64_t)row * a.q_srow + (int64_t)head * a.q_shead + 8 * h;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            if (D == 256 || valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+            if (valid) qreg[ks].u = *reinterpret_cast<const uint4*>(qp + 16 * ks);
             else qreg[ks].u = make_uint4(0, 0, 0, 0);
         }
-    };
-    if constexpr (D == 128) load_q();
+    }
 
     const int big = 0x7FFFFFFF;
     int lo = big, last = -1;                // empty range for padding pairs
     if (valid) prompt_span(a, row, lo, last);
-    if constexpr (D == 256) load_q();
     // key range of this wave, the range all its valid pairs see, and the workgroup range
     const int w_kmin = wave_min_i(lo);
     const int w_kmax = wave_max_i(last);
     const int w_loall = wave_max_i(valid ? lo : -1);
     const int w_lastall = wave_min_i(valid ? last : big);
     if (lane == 0) { red_i[0][wave] = w_kmin; red_i[1][wave] = w_kmax; }
-    if constexpr (D == 256) lds_barrier();
-    else __syncthreads();
+    __syncthreads();
     int kmin = red_i[0][0], kmax = red_i[1][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) { kmin = min(kmin, red_i[0][w]); kmax = max(kmax, red_i[1][w]); }
@@ -260,8 +252,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
             w_every &= (uint32_t)__shfl_xor((int)w_every, m, 64);
         }
         if (lane == 0) red_sel[wave] = w_any;
-        if constexpr (D == 256) lds_barrier();
-        else __syncthreads();
+        __syncthreads();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) tiles |= red_sel[w];
         if (tiles == 0) return;             // none of the workgroup's rows selected a tile here
@@ -275,17 +266,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
     };
     const int ntiles = sparse ? __builtin_popcount(tiles) : t1 - t0 + 1;
 
-    // First use of the Q^T operand (at d = 256 after the first tile loads are issued): a
-    // negative scale is carried by q's sign (exact), so the exponent factor is positive and
+    // A negative scale is carried by q's sign (exact), so the exponent factor is positive and
     // the row maximum of the raw scores gives the maximum of the scaled ones.
-    auto flip_q = [&]() __attribute__((always_inline)) {
+    {
         const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             qreg[ks].u.x ^= flip; qreg[ks].u.y ^= flip; qreg[ks].u.z ^= flip; qreg[ks].u.w ^= flip;
         }
-    };
-    if constexpr (D == 128) flip_q();
+    }
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -516,26 +505,6 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av.v, plo.v, oacc[db], 0, 0, 0);
             }
         }
-        if constexpr (D == 256) {
-            // keep the order: step 0's reads, then each step's MFMAs with the next step's
-            // reads spread among them
-            // (16 reads a step: two after each MFMA with one part, one with two parts, two
-            // after every three with three parts)
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 2);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const bool more = s + 1 < 4;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                    if (NP == 1 && more) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-                    if (NP >= 2 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-                    if (NP >= 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                    if (NP == 2 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-                    if (NP == 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                    if (NP == 3 && more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-                }
-        }
     };
     auto finish = [&](int tile, f32x16 (&sacc)[2], const char* vt) __attribute__((always_inline)) {
         const Soft sf = soft_head(tile, sacc, is_full(tile));
@@ -562,10 +531,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         __syncthreads();
     };
 
-    // unsplit dense prompts at d = 128 (the long ones) walk their tiles software-pipelined
-    // (this kernel sees d = 256 only for sparse prompts: dense ones take prompt_quarter.h)
-    bool piped = false;
-    if constexpr (D == 128) piped = !split && !sparse;
+    // unsplit dense prompts (the long ones) walk their tiles software-pipelined
+    const bool piped = !split && !sparse;
     if (piped) {
         // A software-pipelined walk. While tile t's
         // softmax runs on the VALU, tile t + 1's scores are already on the matrix cores; K is
@@ -586,7 +553,6 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         issue_half(t0, Ks0, kg);
         issue_half(t0, Vs0, vg);
         if (t0 + 1 <= t1) issue_half(t0 + 1, Ks1, kg);
-        if constexpr (D == 256) flip_q();
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (meets(t0)) scores(Ks0, sa);
@@ -597,7 +563,6 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void prompt_kernel(Prom
         }
     } else {
         issue_tile(tile_at(0), Ks0, Vs0);
-        if constexpr (D == 256) flip_q();
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int i = 0; i < ntiles; i += 2) {

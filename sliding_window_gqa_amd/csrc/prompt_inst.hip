@@ -1,5 +1,5 @@
-// One instantiation of the prompt kernel (prompt_impl.h): head dim WA_INST_D with P in
-// WA_INST_NP bf16 parts, and at head dim 256 the quarter-tile kernel of dense prompts
+// One instantiation of the prompt kernels with P in WA_INST_NP bf16 parts: at head dim 128 the
+// 128-pair kernel (prompt_impl.h), at head dim 256 the quarter-tile kernel of dense prompts
 // (prompt_quarter.h) and the row-group kernel of block-sparse prompts (prompt_sparse.h); with
 // WA_INST_POST also the merge and check kernels at that head dim.
 // The build compiles this file once per variant the launcher in prompt.hip calls, so that
@@ -17,9 +17,11 @@
 
 namespace wa {
 
+#if WA_INST_D == 128
 hipError_t WA_MAIN(WA_INST_D, WA_INST_NP)(const PromptArgs& b, int nblk, unsigned grid, hipStream_t s) {
     return launch_main<WA_INST_D, WA_INST_NP>(b, nblk, grid, s);
 }
+#endif
 
 #if WA_INST_D == 256
 #define WA_QUARTER(np) WA_CAT2(launch_prompt_quarter_, np)
