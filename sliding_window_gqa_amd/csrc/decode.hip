@@ -14,19 +14,23 @@
 //   scores  per lane: 8-dim partial dot products with v_dot2_f32_bf16 (bf16 pairs, fp32
 //           accumulate), then a transposing sum over the run's lanes (DPP quad permutes and
 //           row mirrors, a swizzle for the 16-lane step) that leaves each key's score in one
-//           lane: 16 keys per reduction, no partial sum kept longer than needed.
+//           lane: 8 keys per reduction up to four query heads a key head, 16 beyond; no
+//           partial sum kept longer than needed.
 //   softmax one wave per query head: 4 keys per lane, wave butterflies for max and sum.
 //   P.V     fp32 on the VALU: each run is an fma chain in key order over its keys, 8 dims a
 //           lane; the runs are summed in run order through LDS.
-//   loads   K and V arrive in 16-key units (16 x 16 bytes per lane) through one register
-//           buffer, refilled with the next unit as soon as it is consumed (16 loads a lane
-//           in flight; 32, through two buffers, streamed slower).
-//   kernels decode_kernel<.., false>: one workgroup per (row, key head, chunk), partials to
-//           memory, then merge_kernel; decode_kernel<.., true>: for large batches of rows
-//           that do not share rings, one workgroup per (row, key head) walks the row's
+//   loads   K and V arrive in units of 8 keys (8 x 16 bytes per lane) for large grids, at
+//           most 64 registers so that eight workgroups share a CU, or of 16 or 32 keys (fewer
+//           round trips) for small grids, through one register buffer that is
+//           refilled with the next unit as soon as it is consumed; a second buffer (twice the
+//           loads in flight) streamed slower.
+//   kernels decode_kernel<.., false, ..>: one workgroup per (row, key head, chunk), partials
+//           to memory, then merge_kernel; decode_kernel<.., true, 8>: for large batches of
+//           rows that do not share rings, one workgroup per (row, key head) walks the row's
 //           chunks and merges them itself.
-//           Both run the same per-chunk code and the same merge arithmetic, so a row's bits
-//           do not depend on which one ran it (nor on the batch, the slot or the ring size).
+//           All run the same per-chunk arithmetic (the load unit sets only the loads in
+//           flight) and the same merge arithmetic, so a row's bits do not depend on which one
+//           ran it (nor on the batch, the slot or the ring size).
 //   grid    workgroup ids remapped so that each XCD works on the rows of a few key heads and
 //           their rings stay in its L2.
 //
@@ -46,6 +50,16 @@ hipError_t launch_decode_kernel_256_2(const DecodeArgs&, unsigned, hipStream_t);
 hipError_t launch_decode_kernel_256_4(const DecodeArgs&, unsigned, hipStream_t);
 hipError_t launch_decode_kernel_256_8(const DecodeArgs&, unsigned, hipStream_t);
 hipError_t launch_decode_kernel_256_16(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_128_1(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_128_2(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_128_4(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_128_8(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_128_16(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_256_1(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_256_2(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_256_4(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_256_8(const DecodeArgs&, unsigned, hipStream_t);
+hipError_t launch_decode_small_256_16(const DecodeArgs&, unsigned, hipStream_t);
 hipError_t launch_decode_whole_256_1(const DecodeArgs&, unsigned, hipStream_t);
 hipError_t launch_decode_whole_256_2(const DecodeArgs&, unsigned, hipStream_t);
 
@@ -156,10 +170,29 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
     }
 }
 
+// Chunk grids below this many workgroups (under four a CU) load 16-key units: fewer round
+// trips per chunk; larger grids load 8-key units and fit seven workgroups a CU. The
+// arithmetic is the same.
+constexpr unsigned kSmallGrid = 1024;
+
 template <int D>
 hipError_t launch_part_d(const DecodeArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
     const unsigned grid = (unsigned)(a.C * a.hkv * a.rows);
+    if (grid < kSmallGrid) {
+        if (D == 256) {
+            if (G <= 1) return launch_decode_small_256_1(a, grid, s);
+            if (G <= 2) return launch_decode_small_256_2(a, grid, s);
+            if (G <= 4) return launch_decode_small_256_4(a, grid, s);
+            if (G <= 8) return launch_decode_small_256_8(a, grid, s);
+            return launch_decode_small_256_16(a, grid, s);
+        }
+        if (G <= 1) return launch_decode_small_128_1(a, grid, s);
+        if (G <= 2) return launch_decode_small_128_2(a, grid, s);
+        if (G <= 4) return launch_decode_small_128_4(a, grid, s);
+        if (G <= 8) return launch_decode_small_128_8(a, grid, s);
+        return launch_decode_small_128_16(a, grid, s);
+    }
     if (D == 256) {
         if (G <= 1) return launch_decode_kernel_256_1(a, grid, s);
         if (G <= 2) return launch_decode_kernel_256_2(a, grid, s);

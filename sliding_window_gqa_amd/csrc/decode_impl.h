@@ -14,19 +14,23 @@
 //   scores  per lane: 8-dim partial dot products with v_dot2_f32_bf16 (bf16 pairs, fp32
 //           accumulate), then a transposing sum over the run's lanes (DPP quad permutes and
 //           row mirrors, a swizzle for the 16-lane step) that leaves each key's score in one
-//           lane: 16 keys per reduction, no partial sum kept longer than needed.
+//           lane: 8 keys per reduction up to four query heads a key head, 16 beyond; no
+//           partial sum kept longer than needed.
 //   softmax one wave per query head: 4 keys per lane, wave butterflies for max and sum.
 //   P.V     fp32 on the VALU: each run is an fma chain in key order over its keys, 8 dims a
 //           lane; the runs are summed in run order through LDS.
-//   loads   K and V arrive in 16-key units (16 x 16 bytes per lane) through one register
-//           buffer, refilled with the next unit as soon as it is consumed (16 loads a lane
-//           in flight; 32, through two buffers, streamed slower).
-//   kernels decode_kernel<.., false>: one workgroup per (row, key head, chunk), partials to
-//           memory, then merge_kernel; decode_kernel<.., true>: for large batches of rows
-//           that do not share rings, one workgroup per (row, key head) walks the row's
+//   loads   K and V arrive in units of 8 keys (8 x 16 bytes per lane) for large grids, at
+//           most 64 registers so that eight workgroups share a CU, or of 16 or 32 keys (fewer
+//           round trips) for small grids, through one register buffer that is
+//           refilled with the next unit as soon as it is consumed; a second buffer (twice the
+//           loads in flight) streamed slower.
+//   kernels decode_kernel<.., false, ..>: one workgroup per (row, key head, chunk), partials
+//           to memory, then merge_kernel; decode_kernel<.., true, 8>: for large batches of
+//           rows that do not share rings, one workgroup per (row, key head) walks the row's
 //           chunks and merges them itself.
-//           Both run the same per-chunk code and the same merge arithmetic, so a row's bits
-//           do not depend on which one ran it (nor on the batch, the slot or the ring size).
+//           All run the same per-chunk arithmetic (the load unit sets only the loads in
+//           flight) and the same merge arithmetic, so a row's bits do not depend on which one
+//           ran it (nor on the batch, the slot or the ring size).
 //   grid    workgroup ids remapped so that each XCD works on the rows of a few key heads and
 //           their rings stay in its L2.
 //
@@ -91,6 +95,12 @@ __device__ __forceinline__ int xcd_logical(int L, int total) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// a compile-time index for the written-out unit steps
+template <int N>
+struct Int {
+    static constexpr int value = N;
+};
+
 // 2-element bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
@@ -124,38 +134,66 @@ __device__ __forceinline__ void halve(const float (&in)[2 * N], float (&out)[N],
     }
 }
 
-// Sum over the LPK lanes of a run of 16 per-lane partials v[i] (key i of a 16-key unit):
-// lane dl ends with the full sum of key dl >> 1 (LPK = 32, lanes dl and dl ^ 1 agree) or
-// key dl (LPK = 16). A fixed tree: the bits of a key never depend on the data.
-template <int LPK>
-__device__ __forceinline__ float unit_sum(const float (&v)[16], int dl) {
-    float a8[8], a4[4], a2[2], a1[1];
-    if constexpr (LPK == 32) {
-        halve<16, 8>(v, a8, dl);
-        halve<8, 4>(a8, a4, dl);
-        halve<4, 2>(a4, a2, dl);
-        halve<2, 1>(a2, a1, dl);
-        return a1[0] + partner<1>(a1[0]);
+// Sum over the LPK lanes of a run of TK per-lane partials v[i] (key i of a TK-key unit, TK =
+// 8 or 16). TK = 16: lane dl ends with the full sum of key dl >> 1 (LPK = 32; lanes dl and
+// dl ^ 1 agree) or key dl (LPK = 16). TK = 8: key dl >> 2 (LPK = 32; lanes dl .. dl ^ 3
+// agree) or key dl >> 1 (LPK = 16; lanes dl and dl ^ 1 agree). A fixed tree: the bits of a
+// key never depend on the data.
+template <int LPK, int TK>
+__device__ __forceinline__ float unit_sum(const float (&v)[TK], int dl) {
+    static_assert(LPK == 32 || LPK == 16, "8 dims a lane at d = 128 or 256");
+    if constexpr (TK == 16) {
+        float a8[8], a4[4], a2[2], a1[1];
+        if constexpr (LPK == 32) {
+            halve<16, 8>(v, a8, dl);
+            halve<8, 4>(a8, a4, dl);
+            halve<4, 2>(a4, a2, dl);
+            halve<2, 1>(a2, a1, dl);
+            return a1[0] + partner<1>(a1[0]);
+        } else {
+            halve<8, 8>(v, a8, dl);
+            halve<4, 4>(a8, a4, dl);
+            halve<2, 2>(a4, a2, dl);
+            halve<1, 1>(a2, a1, dl);
+            return a1[0];
+        }
     } else {
-        static_assert(LPK == 16, "8 dims a lane at d = 128 or 256");
-        halve<8, 8>(v, a8, dl);
-        halve<4, 4>(a8, a4, dl);
-        halve<2, 2>(a4, a2, dl);
-        halve<1, 1>(a2, a1, dl);
-        return a1[0];
+        static_assert(TK == 8, "units of 8 or 16 keys");
+        float a4[4], a2[2], a1[1];
+        if constexpr (LPK == 32) {
+            halve<16, 4>(v, a4, dl);
+            halve<8, 2>(a4, a2, dl);
+            halve<4, 1>(a2, a1, dl);
+            const float s = a1[0] + partner<2>(a1[0]);
+            return s + partner<1>(s);
+        } else {
+            halve<8, 4>(v, a4, dl);
+            halve<4, 2>(a4, a2, dl);
+            halve<2, 1>(a2, a1, dl);
+            return a1[0] + partner<1>(a1[0]);
+        }
     }
 }
 
-template <int D, int GMAX, bool WHOLE>
-__global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3) void decode_kernel(DecodeArgs a) {
+template <int D, int GMAX, bool WHOLE, int UK>
+__global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2
+                                      : UK == 8 ? (GMAX <= 2 ? 8 : 4)
+                                      : UK == 16 ? (GMAX <= 2 ? 4 : 3) : 2) void decode_kernel(DecodeArgs a) {
     constexpr int LPK = D / 8;               // lanes per key: 8 dims a lane
     constexpr int NRUN = kThreads / LPK;     // runs of consecutive keys per chunk
     constexpr int RUNLEN = kChunk / NRUN;    // keys per run
-    constexpr int NU = RUNLEN / 16;          // 16-key load units per run, for K and for V
+    // TK-key units of the lane tree and the fma chains: 8 keys up to four query heads a key
+    // head, 16 beyond (fewer live partials a head); UK-key load units, UK >= TK
+    constexpr int TK = GMAX <= 4 ? 8 : 16;
+    constexpr int NU = RUNLEN / TK;          // tree units per run
+    constexpr int NL = RUNLEN / UK;          // load units per run, for K and for V
+    constexpr int HU = UK / TK;              // tree units per load unit
     constexpr int GH = GMAX < 4 ? GMAX : 4;  // heads per LDS reduction pass
     constexpr int CM = WHOLE ? kRowCMax : 1;
     static_assert(!WHOLE || (D == 256 && GMAX <= 2), "whole rows: d = 256, at most two query heads per key head");
-    static_assert(NU == 1 || NU == 2, "runs of 16 or 32 keys");
+    static_assert(RUNLEN == 16 || RUNLEN == 32, "runs of 16 or 32 keys");
+    static_assert((UK == 8 || UK == 16 || UK == 32) && UK >= TK && UK <= RUNLEN,
+                  "load units of 8, 16 or 32 keys, whole tree units within a run");
 
     __shared__ float sc[GMAX][kChunk];
     __shared__ float red[NRUN][GH][D];
@@ -207,9 +245,9 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
     auto ld16 = [](__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, (int)soff, 0));
     };
-    // A load unit is 16 keys starting at an absolute position that is a multiple of 16; in
-    // a ring whose length is a multiple of 16 such a unit never wraps, so its keys are one
-    // lane offset plus the key step i * slot bytes in the instruction's scalar offset.
+    // A load unit is UK (8 or 16) keys starting at an absolute position that is a multiple of
+    // UK; in a ring whose length is a multiple of 16 such a unit never wraps, so its keys are
+    // one lane offset plus the key step i * slot bytes in the instruction's scalar offset.
     const bool aligned = WHOLE || (a.ring & 15) == 0;
     const bool big_ring = WHOLE || a.ring >= kChunk;
 
@@ -245,25 +283,29 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
     }
     __syncthreads();
 
-    // Load unit u of a chunk: u < NU are K units, u >= NU V units; unit b of either covers
-    // keys run*RUNLEN + 16 b .. + 15 of the run. Every unit issues its 16 loads (a run with
-    // no visible key reads the head's first row instead), so the loads in flight after each
-    // unit are fixed and every wait covers exactly the unit about to be consumed. Keys of a
-    // run outside the row's range are fetched (their slots are in the ring) and ignored.
+    // Load unit u of a chunk: u < NL are K units, u >= NL V units; unit b of either covers
+    // keys run*RUNLEN + UK b .. + UK - 1 of the run and fills the register buffer, which is
+    // refilled with the next unit as soon as the unit has been consumed. Every unit issues its
+    // UK loads (a run with no visible key reads the head's first row instead), so the loads in
+    // flight are fixed and every wait covers exactly the unit about to be consumed. Keys of a
+    // run outside the row's range are fetched (their slots are in the ring) and ignored. The
+    // load unit sets only how many loads a wave has in flight, never the arithmetic, which
+    // works on TK-key tree units: 8-key load units let seven workgroups share a CU (more waves
+    // to cover the L2 latency of shared keys), 16-key ones cut the round trips of a small grid.
     struct Unit {
         uint32_t vo;     // lane offset of the unit's first key (aligned rings)
         int s0;          // ring slot of the unit's first key
-        bool on;         // the run holds a visible key (else the loads read ring slots 0..15)
+        bool on;         // the run holds a visible key (else the loads read the first slots)
         bool isv;
     };
     auto unit_of = [&](const Chunk& ch, int u, bool want) {
         Unit un;
-        un.isv = u >= NU;
-        const int b = un.isv ? u - NU : u;
+        un.isv = u >= NL;
+        const int b = un.isv ? u - NL : u;
         const int r0 = max(run * RUNLEN, ch.kbase);
         const int r1 = min(run * RUNLEN + RUNLEN, ch.kbase + ch.nk);
         un.on = want && r0 < r1;
-        un.s0 = un.on ? slot_of(ch, run * RUNLEN + 16 * b) : 0;
+        un.s0 = un.on ? slot_of(ch, run * RUNLEN + UK * b) : 0;
         un.vo = (uint32_t)un.s0 * sslot_b + 16u * dl;
         return un;
     };
@@ -274,32 +316,34 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
         sl = big_ring ? (sl >= a.ring ? sl - a.ring : sl) : sl % a.ring;
         return ld16(rsrc, (uint32_t)sl * sslot_b + 16u * dl, 0u);
     };
-    auto issue = [&](const Chunk& ch, int u, bool want, uint4 (&B)[16]) {
+    auto issue = [&](const Chunk& ch, int u, bool want, uint4 (&B)[UK]) __attribute__((always_inline)) {
         const Unit un = unit_of(ch, u, want);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) B[i] = load_key(un, i);
+        for (int i = 0; i < UK; ++i) B[i] = load_key(un, i);
     };
     // (The per-unit lambdas are always inlined: at 16 query heads a key head the compiler
     // otherwise left the head loops rolled and kept the accumulators in scratch memory.)
-    // Scores of K unit b: s = scale * (q . k) for every head of the group, into sc.
-    auto consume_k = [&](const Chunk& ch, int b, const uint4 (&B)[16]) __attribute__((always_inline)) {
-        const int key = LPK == 32 ? (dl >> 1) : dl;
-        const bool writer = LPK == 32 ? (dl & 1) == 0 : true;
-        const int kk = run * RUNLEN + 16 * b + key;
+    // Scores of the run's tree unit b (buffer entries o .. o + TK - 1): s = scale * (q . k)
+    // for every head of the group, into sc.
+    auto consume_k = [&](const Chunk& ch, int b, const uint4 (&B)[UK], int o) __attribute__((always_inline)) {
+        const int key = TK == 16 ? (LPK == 32 ? (dl >> 1) : dl) : (LPK == 32 ? (dl >> 2) : (dl >> 1));
+        const bool writer = TK == 16 ? (LPK == 32 ? (dl & 1) == 0 : true)
+                                     : (LPK == 32 ? (dl & 3) == 0 : (dl & 1) == 0);
+        const int kk = run * RUNLEN + TK * b + key;
         const bool vis = writer && kk >= ch.kbase && kk < ch.kbase + ch.nk;
 #pragma unroll
         for (int h = 0; h < GMAX; ++h) {
             if (h < G) {
                 const uint4 qv = *reinterpret_cast<const uint4*>(&qs[h][8 * dl]);
-                float v[16];
+                float v[TK];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s = dot2(qv.x, B[i].x, 0.f);
-                    s = dot2(qv.y, B[i].y, s);
-                    s = dot2(qv.z, B[i].z, s);
-                    v[i] = dot2(qv.w, B[i].w, s);
+                for (int i = 0; i < TK; ++i) {
+                    float s = dot2(qv.x, B[o + i].x, 0.f);
+                    s = dot2(qv.y, B[o + i].y, s);
+                    s = dot2(qv.z, B[o + i].z, s);
+                    v[i] = dot2(qv.w, B[o + i].w, s);
                 }
-                const float s = unit_sum<LPK>(v, dl);
+                const float s = unit_sum<LPK, TK>(v, dl);
                 if (vis) sc[h][kk] = a.scale * s;
             }
         }
@@ -317,38 +361,47 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
             }
         }
     };
-    // P.V of V unit b: fma chains in key order over the run's visible keys
-    auto consume_v = [&](const Chunk& ch, int b, const uint4 (&B)[16]) __attribute__((always_inline)) {
+    // P.V of the run's tree unit b (buffer entries o .. o + TK - 1): fma chains in key order
+    // over the run's visible keys
+    auto consume_v = [&](const Chunk& ch, int b, const uint4 (&B)[UK], int o) __attribute__((always_inline)) {
         const int r0 = max(run * RUNLEN, ch.kbase);
         const int r1 = min(run * RUNLEN + RUNLEN, ch.kbase + ch.nk);
         if (r0 == run * RUNLEN && r1 == run * RUNLEN + RUNLEN) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) fold_key(B[i], run * RUNLEN + 16 * b + i);
+            for (int i = 0; i < TK; ++i) fold_key(B[o + i], run * RUNLEN + TK * b + i);
         } else if (r0 < r1) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = run * RUNLEN + 16 * b + i;
-                if (kk >= r0 && kk < r1) fold_key(B[i], kk);
+            for (int i = 0; i < TK; ++i) {
+                const int kk = run * RUNLEN + TK * b + i;
+                if (kk >= r0 && kk < r1) fold_key(B[o + i], kk);
             }
         }
     };
 
-    // one register buffer: 16 loads a lane in flight (two buffers, 32 in flight, measured
-    // slower on this part's memory system)
-    uint4 X[16];
+    // one register buffer (two, double the loads in flight, measured slower on this part's
+    // memory system)
+    uint4 X[UK];
     Chunk cur = chunk_at(k0);
     issue(cur, 0, true, X);
     for (int k = k0; k < k0 + nch; ++k) {
         const int ks = k - k0;                   // chunk slot within this workgroup
         const bool more = k + 1 < k0 + nch;
         const Chunk nxt = chunk_at(more ? k + 1 : k);
-        // ---- scores; each consumed unit frees the buffer for the next: K units, then V
-        consume_k(cur, 0, X);
-        if constexpr (NU == 2) {
-            issue(cur, 1, true, X);
-            consume_k(cur, 1, X);
-        }
-        issue(cur, NU, true, X);
+        // ---- scores; each consumed unit frees the buffer for the next: K units, then the
+        // first V unit
+        // (the tree units are written out, not looped over: in a loop the compiler kept more
+        // registers live and spilled at eight or more query heads a key head)
+        auto kstep = [&](auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            if constexpr (b < NU) {
+                consume_k(cur, b, X, TK * (b % HU));
+                if constexpr (b % HU == HU - 1) issue(cur, b / HU + 1, true, X);
+            }
+        };
+        kstep(Int<0>{});
+        kstep(Int<1>{});
+        kstep(Int<2>{});
+        kstep(Int<3>{});
         __syncthreads();
         // ---- chunk softmax: m_c, p = expf(s - m_c), l_c, one wave per head
         for (int h = wave; h < G; h += 4) {
@@ -383,17 +436,26 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
             }
         }
         __syncthreads();
-        // ---- P.V; the freed buffers take the next chunk's K
+        // ---- P.V; the freed buffer takes the remaining V units, then the next chunk's first
+        // K unit
 #pragma unroll
         for (int h = 0; h < GMAX; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        consume_v(cur, 0, X);
-        if constexpr (NU == 2) {
-            issue(cur, NU + 1, true, X);
-            consume_v(cur, 1, X);
-        }
-        if (WHOLE) issue(nxt, 0, more, X);   // the next chunk's first K unit
+        auto vstep = [&](auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            if constexpr (b < NU) {
+                consume_v(cur, b, X, TK * (b % HU));
+                if constexpr (b % HU == HU - 1) {
+                    if constexpr (b / HU + 1 < NL) issue(cur, NL + b / HU + 1, true, X);
+                    else if (WHOLE) issue(nxt, 0, more, X);
+                }
+            }
+        };
+        vstep(Int<0>{});
+        vstep(Int<1>{});
+        vstep(Int<2>{});
+        vstep(Int<3>{});
         // ---- runs summed in run order, GH heads per pass
 #pragma unroll
         for (int hp = 0; hp < GMAX; hp += GH) {
@@ -466,11 +528,11 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2 : GMAX <= 2 ? 5 : 3
     }
 }
 
-// Launch of decode_kernel<D, GMAX, WHOLE> on `grid` workgroups (defined by the file that
+// Launch of decode_kernel<D, GMAX, WHOLE, UK> on `grid` workgroups (defined by the file that
 // instantiates it).
-template <int D, int GMAX, bool WHOLE>
+template <int D, int GMAX, bool WHOLE, int UK>
 hipError_t launch_chunk_kernel(const DecodeArgs& a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<D, GMAX, WHOLE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, GMAX, WHOLE, UK>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
