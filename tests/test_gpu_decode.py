@@ -90,6 +90,30 @@ def test_decode_invariants():
         assert np.array_equal(gu.run_decode(case), full)
 
 
+@pytest.mark.parametrize("rows,hq,hkv,d,win,ring,streams", [
+    (32, 32, 8, 256, 1024, 1536, 2),     # four query heads a key head
+    (40, 24, 8, 256, 700, 1024, 2),      # three
+    (36, 16, 16, 256, 1024, 1536, 2),    # one, d = 256
+    (48, 8, 8, 128, 1024, 1536, 3),      # one, d = 128
+    (40, 16, 8, 128, 1024, 1536, 3),     # two, d = 128
+])
+def test_large_grid_rows_match_rows_alone(rows, hq, hkv, d, win, ring, streams):
+    """Chunk grids of 1,024 workgroups or more (the kernel form with 8-key load units) pass the
+    gate, and a row alone (a small grid: the form with 16- or 32-key load units) gets the same
+    bits: the load unit never changes the arithmetic."""
+    rng = np.random.default_rng(rows * 17 + hq + d)
+    pos = rng.integers(0, 20001, size=rows)
+    pos[:3] = [0, 255, 256]
+    case = workloads.decode_case("large grid", rows, hq, hkv, d, win, ring, streams, pos,
+                                 seed=rows + 5 * hq + d, peak_every=3)
+    full, _ = _gate(case, f"large grid {rows}x{hq}/{hkv}x{d} win{win} ring{ring} streams{streams}")
+    for r in (0, 2, rows // 2, rows - 1):
+        t = int(case.stream[r])
+        one = workloads.DecodeCase("alone", case.q[r:r + 1], case.k[t:t + 1], case.v[t:t + 1],
+                                   np.array([0], np.int32), case.pos[r:r + 1], case.win, case.ring)
+        assert np.array_equal(gu.run_decode(one)[0], full[r]), r
+
+
 @pytest.mark.parametrize("rows,hq,hkv,win,ring,streams", [
     (40, 16, 8, 1536, 1536, 2),    # window = ring: a row's chunks c and c + 6 share a slot block
     (33, 4, 4, 0, 1024, 3),        # linear cache, one query head per key head
