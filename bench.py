@@ -660,8 +660,8 @@ def main():
                                            "interleaved projection buffer",
                                "ms": round(ms, 4), "bytes_per_call": pr.bytes, "gbs": round(gbs, 2)}
         res["roofline_prepare_long"] = roofline(
-            "hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic_bytes("prepare_long", ["prepare_kernel"]),
-            "prepare_kernel<128> (RMSNorm + RoPE 96 dims, bf16 coefficients)")
+            "hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic_bytes("prepare_long", ["prepare_wide_kernel", "prepare_kernel"]),
+            "prepare_wide_kernel<128> (RMSNorm + RoPE 96 dims, bf16 coefficients, 8 dims a lane)")
         del pr
 
     if oracle is not None:

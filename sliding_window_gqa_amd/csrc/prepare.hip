@@ -16,12 +16,18 @@
 // gfx950 mapping: one workgroup of 256 threads per row. The row's R/2 cos/sin pairs are
 // computed once (float64 cos and sin of the fp32 angle, each rounded once to fp32, i.e. a
 // correctly rounded cosf/sinf; the inverse frequencies come computed by the host) into LDS
-// and shared by all heads. Each wave takes heads h = wave, wave + 4, ... and loads a batch
-// of them (14 at d = 128, 8 at d = 256) before computing any: a lane holds
-// D/64 consecutive dims (one 4- or 8-byte load), the lane's cos/sin and partner index are
-// fixed for the row, partners of the rotation come through LDS (one row per batch entry,
-// so the eight heads' chains interleave), the sum of squares is a VALU-only wave sum and
-// the bf16 roundings are hardware conversions (v_cvt_pk_bf16_f32, nearest-even).
+// and shared by all heads; the bf16 roundings are hardware conversions (v_cvt_pk_bf16_f32,
+// nearest-even). Two forms, the same arithmetic per value:
+//   wide    (16-byte aligned rows and heads, R a multiple of 16) a lane holds 8 consecutive
+//           dims of a head (one 16-byte load and store), a head is D/8 lanes, and each wave
+//           requests up to 8 head groups (every head of a 112-head row at d = 128) before
+//           computing any; the head's sum of squares is a lane tree inside its lanes and the
+//           rotation partner is the lane R/16 lanes away (one lane permute per value);
+//   narrow  (anything else) each wave takes heads h = wave, wave + 4, ... and loads a batch
+//           of them (14 at d = 128, 8 at d = 256) before computing any: a lane holds D/64
+//           consecutive dims (one 4- or 8-byte load), partners of the rotation come through
+//           LDS (one row per batch entry, so the heads' chains interleave), the sum of
+//           squares is a VALU-only wave sum.
 #include "wa_common.h"
 
 namespace wa {
@@ -211,10 +217,168 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepArgs a) {
     }
 }
 
+// The same preparation with 8 dims a lane (16-byte loads and stores): a head is D/8 lanes (4
+// heads a wave instruction at d = 128, 2 at d = 256), and a wave requests up to kWideBatch
+// such head groups before computing any, which at d = 128 is every head of a 112-head row.
+// Sums of squares are lane-tree sums inside the head's lanes; the rotation partner of a lane's
+// 8 dims is the lane R/16 lanes away (R a multiple of 16), fetched with one lane permute per
+// value. The arithmetic per value is the 2-dims-a-lane kernel's; only the summation order of
+// the head's sum of squares differs. Needs 16-byte aligned rows and heads.
+constexpr int kWideBatch = 8;
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void prepare_wide_kernel(PrepArgs a) {
+    constexpr int LPH = D / 8;             // lanes a head
+    constexpr int HPI = 64 / LPH;          // heads a wave instruction
+    constexpr int W = kPrepThreads / 64;
+    __shared__ float cs[2][128];           // cos, sin of pair j < R/2 (R <= 256)
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lh = lane % LPH, hsub = lane / LPH;
+    int pos = a.pos_of_row[r];
+    pos = pos < 0 ? 0 : pos;
+    const int R = a.rope_dims, half = R / 2;
+    const uint16_t* xrow = a.x + (int64_t)r * a.x_srow;
+    const int ngroups = (a.heads + HPI - 1) / HPI;
+    auto head_of = [&](int grp) { return grp * HPI + hsub; };
+    auto load_batch = [&](int g0, uint4 (&w)[kWideBatch]) {
+#pragma unroll
+        for (int b = 0; b < kWideBatch; ++b) {
+            const int h = min(head_of(g0 + W * b), a.heads - 1);
+            w[b] = *reinterpret_cast<const uint4*>(xrow + (int64_t)h * a.x_shead + 8 * lh);
+        }
+    };
+    // the first batch's loads are in flight while the row's coefficients are computed
+    uint4 w[kWideBatch];
+    load_batch(wave, w);
+    if (a.mode != kPrepCopy) {
+        for (int j = tid; j < half; j += kPrepThreads) {
+            const float ang = (float)pos * a.inv[j];
+            double sn, cn;
+            sincos((double)ang, &sn, &cn);
+            cs[0][j] = (float)cn;
+            cs[1][j] = (float)sn;
+        }
+    }
+    __syncthreads();
+
+    uint16_t* orow;
+    if (a.ring > 0) {
+        int t = a.stream_of_row[r];
+        t = t < 0 ? 0 : (t >= a.streams ? a.streams - 1 : t);
+        orow = a.out + (int64_t)t * a.o_sstream + (int64_t)(pos % a.ring) * a.o_sslot;
+    } else {
+        orow = a.out + (int64_t)r * a.o_sslot;
+    }
+    // this lane's rotation, fixed for the row: its dims 8 lh .. + 7 all lie below R/2, in
+    // [R/2, R) or past R; y = v c + partner s' with s' = -s below R/2 and +s above (bf16
+    // coefficients in the RMS recipe); the partner lane is R/16 lanes up or down
+    const int d0 = 8 * lh;
+    const bool rotd = d0 < R;
+    const int plane = d0 < half ? lane + half / 8 : (rotd ? lane - half / 8 : lane);
+    float cf[8], sf[8], qsr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        cf[e] = 1.f; sf[e] = 0.f;
+        if (rotd) {
+            const int i = d0 + e;
+            const int j = i < half ? i : i - half;
+            float c = cs[0][j], sn = cs[1][j];
+            if (a.mode == kPrepRmsRope) {
+                c = bf16_to_f32(f32_to_bf16_rne(c));
+                sn = bf16_to_f32(f32_to_bf16_rne(sn));
+            }
+            cf[e] = c;
+            sf[e] = i < half ? -sn : sn;
+        }
+        qsr[e] = a.qs != nullptr ? a.qs[d0 + e] : 1.f;
+    }
+    const bool scaled = a.qs != nullptr;
+    // sum over the head's LPH lanes (lane-tree inside 16-lane rows, then the 32-lane pair of
+    // rows at d = 256), the result in every lane of the head
+    auto head_sum = [&](float v) {
+        v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]
+        v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]
+        v += dpp_mov<0x141>(v);    // row half-mirror
+        v += dpp_mov<0x140>(v);    // row mirror
+        if constexpr (LPH == 32) {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        }
+        return v;
+    };
+    auto partner = [&](float v) { return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * plane, __float_as_int(v))); };
+
+    for (int g0 = wave; g0 < ngroups; g0 += W * kWideBatch) {
+        if (g0 != wave) load_batch(g0, w);
+#pragma unroll
+        for (int b = 0; b < kWideBatch; ++b) {
+            const int grp = g0 + W * b;
+            if (grp >= ngroups) break;
+            const int h = head_of(grp);
+            uint16_t* op = orow + (int64_t)min(h, a.heads - 1) * a.o_shead + d0;
+            uint4 res;
+            if (a.mode == kPrepCopy) {
+                res = w[b];
+            } else {
+                const uint32_t u[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
+                float v[8], f[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = lo_bf16(u[e]);
+                    v[2 * e + 1] = hi_bf16(u[e]);
+                }
+                if (a.mode == kPrepRopeL2) {
+                    // r = bf16(rope(x)); n = bf16(r / sqrt(sum r^2 + eps)); q = bf16(qs * n)
+                    float rr[8], ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = partner(v[e]);
+                        rr[e] = round_bf16(rotd ? fmaf(v[e], cf[e], pv * sf[e]) : v[e]);
+                        ss = fmaf(rr[e], rr[e], ss);
+                    }
+                    const float inv = 1.0f / sqrtf(head_sum(ss) + a.eps);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        f[e] = rr[e] * inv;
+                        if (scaled) f[e] = qsr[e] * round_bf16(f[e]);
+                    }
+                } else {
+                    // n = bf16(x / sqrt(mean x^2 + eps)), then r = bf16(rope(n)), bf16
+                    // coefficients
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+                    const float inv = 1.0f / sqrtf(head_sum(ss) * (1.0f / D) + a.eps);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float n = round_bf16(v[e] * inv);
+                        const float pn = partner(n);
+                        f[e] = rotd ? fmaf(n, cf[e], pn * sf[e]) : n;
+                    }
+                }
+                res = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]),
+                                 pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+            }
+            if (h < a.heads) *reinterpret_cast<uint4*>(op) = res;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prepare(const PrepArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.rows);
+    // 8 dims a lane where rows and heads are 16-byte aligned and the rotation's half-width is
+    // a whole number of lanes; else 2 (d = 128) or 4 (d = 256) dims a lane
+    const bool wide = (((uintptr_t)a.x | (uintptr_t)a.out) & 15) == 0 &&
+                      ((a.x_srow | a.x_shead | a.o_sstream | a.o_sslot | a.o_shead) & 7) == 0 &&
+                      (a.mode == kPrepCopy || a.rope_dims % 16 == 0);
+    if (wide) {
+        if (a.d == 256) hipLaunchKernelGGL((prepare_wide_kernel<256>), grid, dim3(kPrepThreads), 0, s, a);
+        else hipLaunchKernelGGL((prepare_wide_kernel<128>), grid, dim3(kPrepThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.d == 256) hipLaunchKernelGGL((prepare_kernel<256>), grid, dim3(kPrepThreads), 0, s, a);
     else hipLaunchKernelGGL((prepare_kernel<128>), grid, dim3(kPrepThreads), 0, s, a);
     return hipGetLastError();

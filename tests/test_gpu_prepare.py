@@ -117,3 +117,26 @@ def test_repeat_is_bit_identical_and_nan_stays_in_its_head():
     mask = np.ones(b.shape[:2], bool)
     mask[5, 2] = False
     assert np.array_equal(b[mask], a[mask])
+
+
+@pytest.mark.parametrize("mode,d,R", [(P.RMS_ROPE, 128, 40), (P.ROPE_L2, 256, 72)])
+def test_rotation_width_not_whole_lanes(mode, d, R):
+    # R not a multiple of 16: the partner of a dim is not a whole number of 8-dim lanes away,
+    # so the 2- or 4-dims-a-lane form runs; same gate
+    _gate(workloads.prep_case("narrow", 21, 7, d, R, seed=260 + R, with_qs=mode == P.ROPE_L2), mode,
+          f"{mode} d={d} R={R} (narrow form)")
+
+
+def test_head_stride_not_16_byte_aligned():
+    # heads 132 elements apart (264 bytes): not 16-byte aligned, so the narrow form runs; its
+    # bits pass the gate and rows that fit both forms agree with the aligned call's gate too
+    c = workloads.prep_case("stride132", 30, 5, 128, 96, seed=270)
+    rows, heads, d = c.x.shape
+    buf = np.zeros((rows, heads, d + 4), np.uint16)
+    buf[:, :, :d] = c.x
+    dev = torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16).cuda()
+    view = dev[:, :, :d]
+    assert view.stride(1) == d + 4
+    out = gu.host_bits(_run(c, P.RMS_ROPE, x_dev=view))
+    lo, hi = P.interval(P.RMS_ROPE, c.x, c.pos, 96, c.theta)
+    assert P.accept(out, lo, hi).all()
