@@ -87,9 +87,6 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
         const int64_t pr = first + i;
         if (pr >= npairs) break;
         const int r = (int)(pr / a.hq), h = (int)(pr % a.hq);
-        const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
-        int n = rs.c_hi - rs.c_lo + 1;
-        n = n > a.C ? a.C : n;
         const int64_t pi = pr * a.C;      // (r * hq + h) * C
         const float* op = a.o + pi * D + DL * lane;
         // eight chunks' o at a time, chunk c0 + j from chunk c0 (j < cnt)
@@ -108,13 +105,20 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
                 }
             }
         };
-        // the first 64 chunks' (m, l) and the first eight chunks' o are all requested
-        // before any is used: one memory round trip for the common row, not three
+        // the pair's first 64 chunk slots' (m, l) and first eight slots' o are all requested
+        // before the row's position is known (slots past the row's chunk count hold stale
+        // values and are never used), so the common row takes one memory round trip, not two
         float o[8][DL];
-        load8(o, 0, min(n, 8));
+        load8(o, 0, min(a.C, 8));
+        const bool inC = lane < a.C;
+        const float mC = inC ? a.m[pi + lane] : -INFINITY;
+        const float lC = inC ? a.l[pi + lane] : 0.f;
+        const RowSpan rs = row_span(a.pos_of_row, r, a.max_pos, a.window);
+        int n = rs.c_hi - rs.c_lo + 1;
+        n = n > a.C ? a.C : n;
         const bool in0 = lane < n;
-        const float m0 = in0 ? a.m[pi + lane] : -INFINITY;
-        const float l0 = in0 ? a.l[pi + lane] : 0.f;
+        const float m0 = in0 ? mC : -INFINITY;
+        const float l0 = in0 ? lC : 0.f;
         float M = fmaxf(-INFINITY, m0);
         for (int cb = 64; cb < n; cb += 64)
             M = fmaxf(M, cb + lane < n ? a.m[pi + cb + lane] : -INFINITY);
@@ -170,9 +174,9 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
     }
 }
 
-// Chunk grids below this many workgroups (under four a CU) load 16-key units: fewer round
-// trips per chunk; larger grids load 8-key units and fit seven workgroups a CU. The
-// arithmetic is the same.
+// Chunk grids below this many workgroups (under four a CU) load 16- or 32-key units (fewer
+// round trips per chunk); larger grids load 8-key units, which fit eight workgroups a CU.
+// The arithmetic is the same.
 constexpr unsigned kSmallGrid = 1024;
 
 template <int D>
