@@ -245,10 +245,11 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2
     auto ld16 = [](__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, (int)soff, 0));
     };
-    // A load unit is UK (8 or 16) keys starting at an absolute position that is a multiple of
-    // UK; in a ring whose length is a multiple of 16 such a unit never wraps, so its keys are
-    // one lane offset plus the key step i * slot bytes in the instruction's scalar offset.
-    const bool aligned = WHOLE || (a.ring & 15) == 0;
+    // A load unit is UK (8, 16 or 32) keys starting at an absolute position that is a
+    // multiple of UK; in a ring whose length is a multiple of UK such a unit never wraps, so
+    // its keys are one lane offset plus the key step i * slot bytes in the instruction's
+    // scalar offset (the whole-row kernel's rings are multiples of 16, its units 8 keys).
+    const bool aligned = WHOLE || (a.ring & (UK - 1)) == 0;
     const bool big_ring = WHOLE || a.ring >= kChunk;
 
     struct Chunk {

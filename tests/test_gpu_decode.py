@@ -114,6 +114,33 @@ def test_large_grid_rows_match_rows_alone(rows, hq, hkv, d, win, ring, streams):
         assert np.array_equal(gu.run_decode(one)[0], full[r]), r
 
 
+@pytest.mark.parametrize("rows,hq,hkv,d,ring", [
+    (3, 4, 2, 256, 1552),     # ring = 16 mod 32: a 32-key unit of a small grid can wrap
+    (40, 16, 8, 256, 1552),   # the same ring under a large grid (8-key units)
+    (3, 4, 2, 256, 1544),     # ring = 8 mod 16
+    (3, 2, 2, 128, 1040),     # d = 128, ring = 16 mod 32
+])
+def test_rings_not_a_multiple_of_the_load_unit(rows, hq, hkv, d, ring):
+    """Rings whose length is a multiple of 16 but not of 32 (or of 8 but not 16): keys of a
+    load unit wrap round the ring end and must come from the ring's first slots; rows whose
+    windows cross the wrap pass the gate and match their bits alone."""
+    rng = np.random.default_rng(ring + rows)
+    pos = rng.integers(ring, 20000, size=rows)
+    # positions whose windows hold a load unit that wraps round the ring end (at rings 1552
+    # and 1544; at 1040 no unit wraps)
+    pos[0] = ring + 48
+    if rows > 1:
+        pos[1] = ring + 300
+    case = workloads.decode_case("wrap", rows, hq, hkv, d, 1024, ring, 2, pos,
+                                 seed=ring + hq, peak_every=2)
+    full, _ = _gate(case, f"ring {ring} rows {rows} {hq}/{hkv}x{d}")
+    for r in (0, rows - 1):
+        t = int(case.stream[r])
+        one = workloads.DecodeCase("alone", case.q[r:r + 1], case.k[t:t + 1], case.v[t:t + 1],
+                                   np.array([0], np.int32), case.pos[r:r + 1], case.win, case.ring)
+        assert np.array_equal(gu.run_decode(one)[0], full[r]), r
+
+
 @pytest.mark.parametrize("rows,hq,hkv,win,ring,streams", [
     (40, 16, 8, 1536, 1536, 2),    # window = ring: a row's chunks c and c + 6 share a slot block
     (33, 4, 4, 0, 1024, 3),        # linear cache, one query head per key head
