@@ -304,7 +304,10 @@ int wa_prepare(const wa_prep_t* p,
     if ((x_srow | x_shead | o_sstream | o_sslot | o_shead) & (int64_t)(al / 2 - 1)) return WA_EARG;
     if (qs && ((uintptr_t)qs & 3)) return WA_EARG;
     wa::PrepArgs a{};
-    a.mode = p->mode; a.rope_dims = p->rope_dims; a.theta = p->theta; a.eps = p->eps;
+    // a copy rotates nothing: its rope_dims is not checked above and must not index the
+    // kernels' cos/sin table
+    a.mode = p->mode; a.rope_dims = p->mode == WA_PREP_COPY ? 0 : p->rope_dims;
+    a.theta = p->theta; a.eps = p->eps;
     // the inverse frequencies depend on j only: computed once here, in float64 and rounded
     // once to fp32, instead of on every row of the kernel
     if (p->mode != WA_PREP_COPY)
