@@ -250,7 +250,10 @@ typedef struct wa_prep {
  * point named in the mode rounds to bf16, nearest-even.
  * Device preconditions: pos >= 0 (negative values are taken as 0), 0 <= stream_of_row[r]
  * < streams (clamped). x and out 8-byte aligned (4-byte at d = 128), strides multiples of 4
- * (2 at d = 128). Errors: WA_EARG, WA_EUNSUPPORTED (d other than 128 or 256), WA_EHIP.
+ * (2 at d = 128); with x and out 16-byte aligned, strides multiples of 8 and rope_dims a
+ * multiple of 16 (or a copy) the call takes a faster form (16-byte accesses), same results
+ * within the stated roundings. Errors: WA_EARG, WA_EUNSUPPORTED (d other than 128 or 256),
+ * WA_EHIP.
  */
 int wa_prepare(const wa_prep_t* p,
                const uint16_t* x, int64_t x_srow, int64_t x_shead,
