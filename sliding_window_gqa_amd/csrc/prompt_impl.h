@@ -671,13 +671,17 @@ __global__ __launch_bounds__(D) void prompt_merge_kernel(PromptArgs a) {
             }
         };
         // chunks in blocks of 64, lane c of a block holding chunk (m, l); the first block's
-        // (m, l) and its first eight chunks' o are requested before any is used
+        // (m, l) and its first eight chunks' o are requested together with the mask words
+        // that tell which are present (slots of absent chunks hold stale values, never used)
+        float o[8][DL];
+        load8(o, 0, min(nc, 8), ~0ull);
+        const bool inr = lane < nc;
+        const float mr = inr ? a.pm[pi + lane] : -INFINITY;
+        const float lr = inr ? a.pl[pi + lane] : 0.f;
         const bool in0 = present(lane);
         const uint64_t inmask0 = __ballot(in0);
-        float o[8][DL];
-        load8(o, 0, min(nc, 8), inmask0);
-        const float m0 = in0 ? a.pm[pi + lane] : -INFINITY;
-        const float l0 = in0 ? a.pl[pi + lane] : 0.f;
+        const float m0 = in0 ? mr : -INFINITY;
+        const float l0 = in0 ? lr : 0.f;
         float M = fmaxf(-INFINITY, m0);
         for (int cb = 64; cb < nc; cb += 64)
             M = fmaxf(M, present(cb + lane) ? a.pm[pi + cb + lane] : -INFINITY);
