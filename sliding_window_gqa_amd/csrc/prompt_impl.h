@@ -140,8 +140,36 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // 16 bytes per lane from a buffer descriptor straight into LDS (buffer_load_dwordx4 ... lds):
 // lane i's bytes land at dst + 16 i.
-__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
+// LDS loads issued as inline assembly (they write LDS only, no register): the compiler does not
+// track them, so each wait on them is written out (lds_dma_wait_*, s_waitcnt before the results
+// are read). M0 holds the wave's LDS destination; lane i's 16 bytes land at M0 + 16 i.
+// Volatile statements keep their order among themselves; the waits below also order every
+// memory access around them, so an LDS read and the load that refills its stage stay on either
+// side of a wait.
+__device__ __forceinline__ void lds_dma_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(m0), "s"(rsrc));
+}
+__device__ __forceinline__ void lds_dma_global16(const void* src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0));
+}
+// all but the last 16 (8) vector-memory loads have landed; all have
+__device__ __forceinline__ void lds_dma_wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void lds_dma_wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void lds_dma_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// every LDS read issued so far has returned
+__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// LDS address of a shared-memory pointer, uniform over the wave
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_ptr)p);
+}
+
+// the same from a wave-uniform base address plus a 32-bit lane offset (global_load_lds, saddr
+// form)
+__device__ __forceinline__ void lds_dma_global16_s(const void* base, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(m0));
 }
 
 // Workgroup barrier that waits for this wave's LDS (and scalar) operations only: global loads
@@ -327,15 +355,22 @@ __global__ __launch_bounds__(kThreads, 2) void prompt_kernel(PromptArgs a, int n
         lane_off[i] = (uint32_t)(r * a.kv_sslot + 8 * c) * 2u;
     }
     const int tile_extent = (int)((uint32_t)((BN - 1) * a.kv_sslot) * 2u + 2u * D);
+    // LDS addresses of the four stages and the wave index, uniform (for the load's M0)
+    const uint32_t mK0 = lds_addr(Ks0), mK1 = lds_addr(Ks1), mV0 = lds_addr(Vs0), mV1 = lds_addr(Vs1);
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    auto mstage = [&](const char* p) __attribute__((always_inline)) {
+        return p == Ks0 ? mK0 : p == Ks1 ? mK1 : p == Vs0 ? mV0 : mV1;
+    };
     // loads of one tile of K (or V) into an LDS stage
     auto issue_half = [&](int tile, char* dst, const uint16_t* src) __attribute__((always_inline)) {
+        const uint32_t mdst = mstage(dst);
         const int base = tile * BN;
         const int sbase = ring_slot(a, base);
         if (base >= kmin && base + BN - 1 <= kmax && sbase + BN <= a.ring) {
             const int64_t toff = (int64_t)sbase * a.kv_sslot;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + toff), (short)0, tile_extent, 0x00020000);
 #pragma unroll
-            for (int i = 0; i < NQ / kWaves; ++i) buffer_to_lds16(rs, dst + 1024 * (wave + kWaves * i), lane_off[i]);
+            for (int i = 0; i < NQ / kWaves; ++i) lds_dma_buffer16(rs, lane_off[i], mdst + 1024u * (uwave + kWaves * i));
             return;
         }
 #pragma unroll
@@ -350,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void prompt_kernel(PromptArgs a, int n
             if (a.ring >= BN) slot = slot >= a.ring ? slot - a.ring : slot;
             else slot = jc % a.ring;
             const int64_t off = (int64_t)slot * a.kv_sslot + 8 * c;
-            __builtin_amdgcn_global_load_lds(src + off, (lds_void_ptr)(dst + 1024 * q), 16, 0, 0);
+            lds_dma_global16_s(src, (uint32_t)(off * 2), mdst + 1024u * (uwave + kWaves * i));
         }
     };
     auto issue_tile = [&](int tile, char* kdst, char* vdst) __attribute__((always_inline)) {

@@ -60,31 +60,6 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr int kOctWaves = 8;           // waves of a quarter-tile workgroup (two per SIMD)
 constexpr int kOctThreads = 64 * kOctWaves;
 
-// LDS loads issued as inline assembly (they write LDS only, no register): the compiler does not
-// track them, so each wait on them is written out (lds_dma_wait_*, s_waitcnt before the results
-// are read). M0 holds the wave's LDS destination; lane i's 16 bytes land at M0 + 16 i.
-// Volatile statements keep their order among themselves; the waits below also order every
-// memory access around them, so an LDS read and the load that refills its stage stay on either
-// side of a wait.
-__device__ __forceinline__ void lds_dma_buffer16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(m0), "s"(rsrc));
-}
-__device__ __forceinline__ void lds_dma_global16(const void* src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(m0));
-}
-// all but the last 16 (8) vector-memory loads have landed; all have
-__device__ __forceinline__ void lds_dma_wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
-__device__ __forceinline__ void lds_dma_wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-__device__ __forceinline__ void lds_dma_wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// every LDS read issued so far has returned
-__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// LDS address of a shared-memory pointer, uniform over the wave
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_ptr)p);
-}
-
 template <int NP>
 __global__ __launch_bounds__(kOctThreads, 1) void prompt_quarter_kernel(PromptArgs a, int nblk) {
     constexpr int D = 256;
