@@ -22,7 +22,8 @@
 //           dims of a head (one 16-byte load and store), a head is D/8 lanes, and each wave
 //           requests up to 8 head groups (every head of a 112-head row at d = 128) before
 //           computing any; the head's sum of squares is a lane tree inside its lanes and the
-//           rotation partner is the lane R/16 lanes away (one lane permute per value);
+//           rotation partner is the lane R/16 lanes away (one lane permute per value); loads
+//           and stores are non-temporal (each byte is touched once);
 //   narrow  (anything else) each wave takes heads h = wave, wave + 4, ... and loads a batch
 //           of them (14 at d = 128, 8 at d = 256) before computing any: a lane holds D/64
 //           consecutive dims (one 4- or 8-byte load), partners of the rotation come through
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(PrepArgs a) {
 // value. The arithmetic per value is the 2-dims-a-lane kernel's; only the summation order of
 // the head's sum of squares differs. Needs 16-byte aligned rows and heads.
 constexpr int kWideBatch = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prepare_wide_kernel(PrepArgs a) {
@@ -245,7 +247,8 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_wide_kernel(PrepArgs a) 
 #pragma unroll
         for (int b = 0; b < kWideBatch; ++b) {
             const int h = min(head_of(g0 + W * b), a.heads - 1);
-            w[b] = *reinterpret_cast<const uint4*>(xrow + (int64_t)h * a.x_shead + 8 * lh);
+            const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + (int64_t)h * a.x_shead + 8 * lh));
+            w[b] = make_uint4(t.x, t.y, t.z, t.w);
         }
     };
     // the first batch's loads are in flight while the row's coefficients are computed
@@ -360,7 +363,10 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_wide_kernel(PrepArgs a) 
                 res = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]),
                                  pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
             }
-            if (h < a.heads) *reinterpret_cast<uint4*>(op) = res;
+            if (h < a.heads) {
+                const u32x4 t = {res.x, res.y, res.z, res.w};
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(op));
+            }
         }
     }
 }
