@@ -14,16 +14,18 @@
 // four waves, one a SIMD, all hold the same columns; wave w takes keys 16w .. 16w + 15 of
 // every selected block (its quarter) with a running (m, l, O) of its own, and walks the
 // selected blocks two at a time (a and b; b absent at an odd end):
-//   * K goes from memory straight into registers in the score product's operand layout
-//     (lane l: key l % 16 of the quarter, dims 32 ks + 8 (l / 16) + 0..7), the next two
-//     quarters' loads issued as soon as the score products have read this step's;
+//   * K goes into LDS (one stage a block) by buffer_load ... lds and is read back in the
+//     score product's operand layout (lane l: key l % 16 of the quarter, dims 32 ks +
+//     8 (l / 16) + 0..7); the next step's K loads go out once the score products have read
+//     this step's, one after each 16-dim block of P.V;
 //   * S^T of a quarter (16 keys x 16 columns) is one chain of eight v_mfma_f32_16x16x32_bf16
 //     products; lane l then holds keys 4 (l / 16) + i of column l % 16 for both blocks, and
 //     those eight values, a's four then b's four, are exactly the B operand (32 keys) of a
 //     v_mfma_f32_16x16x32_bf16 P.V product whose A operand puts the same keys in the same
 //     order: the transposing LDS reads (ds_read_b64_tr_b16) of the two blocks' V, side by side;
-//   * V goes into LDS (the transposing reads need it there) by buffer_load ... lds into two
-//     stages of two blocks each, each wave loading only its own 16 rows: no barrier in the walk;
+//   * V goes into LDS the same way (the transposing reads need it there), the next step's V
+//     among the score products; each wave loads only its own 16 rows of every block, so the
+//     walk needs no barrier;
 //   * the column's row maximum and sum span the four lanes l % 16 + 16k: one
 //     v_permlane16_swap and one v_permlane32_swap step;
 //   * after the walk the four states are merged in LDS in wave order (M = max m_w,
