@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kThreads, WHOLE || GMAX > 8 ? 2
     // flight are fixed and every wait covers exactly the unit about to be consumed. Keys of a
     // run outside the row's range are fetched (their slots are in the ring) and ignored. The
     // load unit sets only how many loads a wave has in flight, never the arithmetic, which
-    // works on TK-key tree units: 8-key load units let seven workgroups share a CU (more waves
+    // works on TK-key tree units: 8-key load units let eight workgroups share a CU (more waves
     // to cover the L2 latency of shared keys), 16-key ones cut the round trips of a small grid.
     struct Unit {
         uint32_t vo;     // lane offset of the unit's first key (aligned rings)
