@@ -12,8 +12,9 @@ served from the caches; that figure is reported beside it under its own name.
 
 Also timed in the same run, each with its own roofline object: the tiny decode (absolute
 time), the 31B prompt chunk, the 64-stream decode (no shared keys: the clean HBM shape), the
-long non-windowed prompt (37,810 x 56 x 128, the MFMA-bound shape), P as three bf16 parts,
-the block-sparse slice and the long prompt's q/k preparation.
+long non-windowed prompt (37,810 x 56 x 128, the MFMA-bound shape; P as one bf16, and on the
+same inputs as two halves (p32) and as three parts), the 12B chunk with P as three parts, the
+block-sparse slice and the long prompt's q/k preparation.
 
 The float64 oracle runs on the host cores first (a process pool forked before the GPU is
 touched, one BLAS thread a process): its time per workload is ``cpu_baseline`` and its
@@ -369,6 +370,14 @@ def _three(case):
     return case
 
 
+def _with_p(case, p32):
+    """The same inputs (arrays shared, not copied) with P carried as ``p32``."""
+    import copy
+    c = copy.copy(case)
+    c.p32 = p32
+    return c
+
+
 def profile_driver(names, iters):
     """Run the workloads for profiler passes, after a plain copy of known size."""
     a = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -383,6 +392,7 @@ def profile_driver(names, iters):
             "prompt12b": lambda: Prompter(workloads.prompt_12b()),
             "prompt31b": lambda: Prompter(workloads.prompt_31b()),
             "long": lambda: Prompter(workloads.long_prompt()),
+            "long2": lambda: Prompter(workloads.long_prompt(p32=api.P_TWO)),
             "long3": lambda: Prompter(workloads.long_prompt(p32=api.P_THREE)),
             "prompt12b3": lambda: Prompter(_three(workloads.prompt_12b())),
             "sparse": lambda: SparsePrompter(workloads.sparse_prompt()),
@@ -422,7 +432,7 @@ def main():
     ap.add_argument("--only", default=None,
                     help="profiler driver: run a 256 MiB device copy (counter calibration), then "
                          "each listed workload (decode1, decode12b, decode12b64, prompt12b, "
-                         "prompt12b3, prompt31b, sparse, long, long3, prepare_long) --steps "
+                         "prompt12b3, prompt31b, sparse, long, long2, long3, prepare_long) --steps "
                          "times; no timing, no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -578,17 +588,23 @@ def main():
         "prompt_quarter_kernel<bf16P>, one call (31B prompt chunk: the whole call is this one "
         "kernel)")
 
-    if not args.no_long:
-        lcase = cases["C5"]
-        lp = Prompter(lcase)
-        lu = prompt_units(lcase)
+    def time_long(case):
+        """Mean warm time of the long prompt (a call is ~40-65 ms: caches hold no part of its
+        2 GB working set between calls) and its sampled rows' bits."""
+        lp = Prompter(case)
         lp(); torch.cuda.synchronize()
         tl = Timed()
         for _ in range(args.long_iters):
             with tl:
                 lp()
-        lms = float(np.mean(tl.ms()))
-        gpu_bits["C5"] = lp.bits(sample["C5"])
+        bits = lp.bits(sample["C5"])
+        del lp
+        return float(np.mean(tl.ms())), bits
+
+    if not args.no_long:
+        lcase = cases["C5"]
+        lu = prompt_units(lcase)
+        lms, gpu_bits["C5"] = time_long(lcase)
         ltf = lu["flops"] / (lms * 1e-3) / 1e12
         res["prefill_long"] = {"workload": "long non-windowed prompt 37,810 x 56 x 128, non-causal, bf16 P",
                                "ms": round(lms, 3), "tflops": round(ltf, 2),
@@ -596,7 +612,18 @@ def main():
         res["roofline_prefill_long"] = roofline("mfma", ltf, MFMA_BF16_PEAK_TFS, "TFLOP/s",
                                                 traffic_bytes("long", ["prompt_kernel"]),
                                                 "prompt_kernel<128,bf16P> (long prompt)")
-        del lp
+        # the same inputs with p32 on (P as two bf16 halves), the long prompt's variant
+        lcase2 = _with_p(lcase, api.P_TWO)
+        lu2 = prompt_units(lcase2)
+        l2ms, gpu_bits["C5-p32"] = time_long(lcase2)
+        l2tf = lu2["flops"] / (l2ms * 1e-3) / 1e12
+        res["prefill_long_p32"] = {"workload": "long prompt 37,810 x 56 x 128, non-causal, p32 (P as two bf16 halves)",
+                                   "ms": round(l2ms, 3), "tflops": round(l2tf, 2),
+                                   "flops_per_call": lu2["flops"],
+                                   "flop_accounting": "(2 + 2*2) * d per visible (row, head, key)"}
+        res["roofline_prefill_long_p32"] = roofline(
+            "mfma", l2tf, MFMA_BF16_PEAK_TFS, "TFLOP/s", traffic_bytes("long2", ["prompt_kernel"]),
+            "prompt_kernel<128,p32> (long prompt)")
 
     # P as three bf16 parts (fp32-accurate P.V): the 12B prompt chunk and the long prompt
     tcase3 = _three(workloads.prompt_12b())
@@ -610,15 +637,9 @@ def main():
                                   "flops_per_call": tu["flops"],
                                   "flop_accounting": "(2 + 2*3) * d per visible (row, head, key)"}
     if not args.no_long:
-        lcase3 = workloads.long_prompt(p32=api.P_THREE)
-        lp3 = Prompter(lcase3)
+        lcase3 = _with_p(cases["C5"], api.P_THREE)
         lu3 = prompt_units(lcase3)
-        lp3(); torch.cuda.synchronize()
-        tl3 = Timed()
-        for _ in range(args.long_iters):
-            with tl3:
-                lp3()
-        l3ms = float(np.mean(tl3.ms()))
+        l3ms, gpu_bits["C5-3"] = time_long(lcase3)
         l3tf = lu3["flops"] / (l3ms * 1e-3) / 1e12
         res["prefill_long_three_parts"] = {"workload": "long prompt 37,810 x 56 x 128, non-causal, P as three bf16 parts",
                                            "ms": round(l3ms, 3), "tflops": round(l3tf, 2),
@@ -626,7 +647,6 @@ def main():
         res["roofline_prefill_long_three_parts"] = roofline(
             "mfma", l3tf, MFMA_BF16_PEAK_TFS, "TFLOP/s", traffic_bytes("long3", ["prompt_kernel"]),
             "prompt_kernel<128,3 parts> (long prompt)")
-        del lp3
 
     # block-sparse prompt slice: 64 rows of a 7,900-token prompt, 32 selected 64-key blocks a
     # row, 24/2 heads x 256, P as three parts
@@ -670,8 +690,14 @@ def main():
                "C3": check.E_P_P32, "C4": check.E_P_BF16, "C5": check.E_P_BF16}
         res["parity"] = {name: parity_entry(gpu_bits[name], oracle[name], e_p[name])
                          for name in oracle if name in gpu_bits}
+        # the long prompt's P variants against the same float64 values (P's carrying changes
+        # only the allowance e_P)
+        for name, ep in (("C5-p32", check.E_P_P32), ("C5-3", check.E_P_THREE)):
+            if "C5" in oracle and name in gpu_bits:
+                res["parity"][name] = parity_entry(gpu_bits[name], oracle["C5"], ep)
         res["parity"]["note"] = ("outputs of the timed calls against the float64 oracle; C5: its "
-                                 "seeded sample of 256 rows x 56 heads")
+                                 "seeded sample of 256 rows x 56 heads, with P as one bf16 (C5), "
+                                 "two halves (C5-p32) and three parts (C5-3)")
         secs = {name: round(o["seconds"], 3) for name, o in oracle.items()}
         c2s = oracle["C2"]["seconds"]
         cb = {"value": round(du["unique_bytes"] / c2s / 1e9, 4), "unit": "GB/s", "cores": cores,
