@@ -44,9 +44,20 @@ def test_prompt_31b_bf16p():
 
 
 def test_long_prompt_sampled():
+    """The long prompt at full size on its seeded sample of rows, with P as one bf16 (the
+    default), as two halves (p32, its variant) and as three parts: one float64 reference, three
+    calls on the same inputs; the literal one-step rule is asserted for the last two."""
     case = workloads.long_prompt()
     rows = workloads.long_prompt_sample_rows(case.n)
-    _gate(case, "long prompt 37810x56x128 sampled", rows=rows)
+    x, S, _ = gu.oracle_prompt(case, rows=rows)
+    for p32, name in ((0, "bf16 P"), (1, "p32"), (2, "three parts")):
+        label = f"long prompt 37810x56x128 sampled, {name}"
+        gu.log(f"prompt case: {label} n={case.n} hq={case.hq} d={case.d} p32={p32}")
+        out = gu.run_prompt(case, p32=p32)[rows]
+        rep, ok = gu.compare(out, x, S, e_p(p32), label)
+        assert ok.all()
+        if p32 == 2:
+            assert rep["tier_S_fail"] == 0, rep
 
 
 THREE = 2      # Window.p32 value: P as three bf16 parts
