@@ -31,6 +31,28 @@ def dev_view(buf_dev, view, base_np):
     return torch.as_strided(buf_dev, view.shape, [s // item for s in view.strides], off)
 
 
+def far_slots(arr, slot_elems):
+    """Device copy of a K or V array ([streams, ring, Hkv, d] or [ring, Hkv, d]) whose ring
+    slots lie ``slot_elems`` elements apart, the streams and key heads side by side at the
+    start of each slot: a layout whose slot span reaches the loads' 2^31-byte offset limit
+    with a short ring."""
+    a = np.asarray(arr)
+    if a.ndim == 3:
+        return far_slots(a[None], slot_elems)[0]
+    s, ring, hkv, d = a.shape
+    assert s * hkv * d <= slot_elems and slot_elems % 8 == 0
+    buf = torch.zeros(ring * slot_elems, dtype=torch.bfloat16, device="cuda")
+    view = buf.as_strided((s, ring, hkv, d), (hkv * d, slot_elems, d, 1))
+    view.copy_(dev_bf16(a))
+    return view
+
+
+def limit_slot_stride(span_slots, d):
+    """Largest slot stride (elements, a multiple of 8) for which ``span_slots`` slot strides
+    plus one row of d stay under 2^31 bytes: the largest the library accepts."""
+    return ((2**31 - 2 - 2 * d) // (2 * span_slots)) // 8 * 8
+
+
 def dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 

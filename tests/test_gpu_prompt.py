@@ -9,6 +9,7 @@ calls must leave each row's bits unchanged) and repeatability by byte equality.
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import attend, check
 from sliding_window_gqa_amd import workloads
@@ -331,3 +332,28 @@ def test_mfma_accumulation_under_cancellation(p32):
     gu.log(f"[mfma accumulation p32={p32}] worst |out - x| / S = {worst:.3e} "
            f"= {worst * 2 ** 24:.1f} x 2^-24; allowance 2^-16 = 256 x 2^-24")
     assert check.accept(out, x, S, check.E_P_THREE, "S").all()
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,p32", [(40, 4, 2, 256, True), (40, 4, 2, 256, THREE),
+                                            (40, 2, 2, 128, False)])
+def test_slot_stride_at_the_31_bit_limit(n, hq, hkv, d, p32):
+    """K/V slots as far apart as wa_prompt accepts (a 64-key tile's span a few hundred KB under
+    2^31 bytes): the rows match the oracle and the same ring laid out densely, bit for bit."""
+    from sliding_window_gqa_amd import api
+    p0, win, ring = 100, 24, 64
+    case = workloads.prompt_case("far slots", n, hq, hkv, d, p0, win, ring, seed=n + d, p32=p32,
+                                 peak_every=2)
+    sslot = gu.limit_slot_stride(63, d)
+    label = f"prompt far slots n{n} {hq}/{hkv}x{d} p32={p32} slot stride {sslot}"
+    gu.log(f"prompt case: {label}")
+    k, v = gu.far_slots(case.k, sslot), gu.far_slots(case.v, sslot)
+    assert 63 * k.stride(0) * 2 + 2 * d < 2**31 - 1 < 63 * (k.stride(0) + 8) * 2 + 2 * d
+    out = api.prompt(gu.dev_bf16(case.q), k, v, p0, win, ring, case.scale, p32=p32)
+    torch.cuda.synchronize()
+    bits = gu.host_bits(out)
+    del k, v, out
+    x, S, _ = gu.oracle_prompt(case)
+    _, ok = gu.compare(bits, x, S, e_p(p32), label)
+    assert ok.all()
+    assert np.array_equal(bits, gu.run_prompt(case))
+

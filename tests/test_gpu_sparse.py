@@ -12,6 +12,7 @@ kernel (head dim 128) and meets the oracle's gate where they do not (256).
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import attend, check
 from sliding_window_gqa_amd import workloads
@@ -170,3 +171,25 @@ def test_row_that_sees_no_key_is_nan():
     x, S, _ = gu.oracle_sparse(case)
     assert np.isnan(x[7]).all()
     assert check.accept(out, x, S, E_P[2]).all()
+
+
+def test_sparse_slot_stride_at_the_31_bit_limit():
+    """The block-sparse prompt (d = 256) with its slots as far apart as wa_prompt_sparse
+    accepts, against the oracle and the dense layout."""
+    from sliding_window_gqa_amd import api
+    d = 256
+    case = workloads.sparse_prompt_case("far slots sparse", 28, 4, 2, d, 100, 2, seed=29)
+    sslot = gu.limit_slot_stride(63, d)
+    label = f"sparse far slots slot stride {sslot}"
+    gu.log(f"prompt case: {label}")
+    k, v = gu.far_slots(case.k, sslot), gu.far_slots(case.v, sslot)
+    m = torch.from_numpy(np.ascontiguousarray(case.masks).view(np.int32)).cuda()
+    out = api.prompt_sparse(gu.dev_bf16(case.q), k, v, case.p0, case.win, case.ring, m, case.scale,
+                            p32=case.p32)
+    torch.cuda.synchronize()
+    bits = gu.host_bits(out)
+    del k, v, out
+    x, S, _ = gu.oracle_sparse(case)
+    _, ok = gu.compare(bits, x, S, E_P[int(case.p32)], label)
+    assert ok.all()
+    assert np.array_equal(bits, gu.run_sparse(case))
