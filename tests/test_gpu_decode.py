@@ -376,23 +376,24 @@ def test_fp32_accumulation_under_cancellation():
     assert check.accept(out, x, S, E_P, "S").all()
 
 
-@pytest.mark.parametrize("rows,win,ring,streams", [
-    (5, 64, 64, 2),         # small chunk grid
-    (600, 64, 256, 3),      # large chunk grid (1,200 workgroups), rings shared by rows
-    (256, 64, 256, 256),    # whole rows: 256 rows, each in its own stream
+@pytest.mark.parametrize("rows,win,ring,streams,d", [
+    (5, 64, 64, 2, 256),        # small chunk grid
+    (5, 64, 64, 2, 128),
+    (600, 64, 256, 3, 256),     # large chunk grid (1,200 workgroups), rings shared by rows
+    (1100, 64, 256, 3, 128),
+    (256, 64, 256, 256, 256),   # whole rows: 256 rows, each in its own stream
 ])
-def test_slot_stride_at_the_31_bit_limit(rows, win, ring, streams):
+def test_slot_stride_at_the_31_bit_limit(rows, win, ring, streams, d):
     """K/V slots as far apart as wa_decode accepts (the ring's span a few hundred KB under
     2^31 bytes): the rows match the oracle and the same rings laid out densely, bit for bit."""
     from sliding_window_gqa_amd import api
-    d = 256
     rng = np.random.default_rng(rows + ring)
     pos = rng.integers(0, 5000, size=rows)
     pos[0] = 0
     case = workloads.decode_case("far slots", rows, 2, 1, d, win, ring, streams, pos,
                                  seed=rows + 7, peak_every=2)
     sslot = gu.limit_slot_stride(ring - 1, d)
-    label = f"decode far slots {rows} rows ring{ring} streams{streams} slot stride {sslot}"
+    label = f"decode far slots {rows} rows x{d} ring{ring} streams{streams} slot stride {sslot}"
     gu.log(f"decode case: {label}")
     k, v = gu.far_slots(case.k, sslot), gu.far_slots(case.v, sslot)
     assert (ring - 1) * k.stride(1) * 2 + 2 * d < 2**31 - 1 < (ring - 1) * (k.stride(1) + 8) * 2 + 2 * d
