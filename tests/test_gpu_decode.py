@@ -406,3 +406,16 @@ def test_slot_stride_at_the_31_bit_limit(rows, win, ring, streams, d):
     _, ok = gu.compare(bits, x, S, E_P, label)
     assert ok.all()
     assert np.array_equal(bits, gu.run_decode(case))
+
+
+@pytest.mark.parametrize("scale", [-0.8, 0.0])
+@pytest.mark.parametrize("d", [256, 128])
+def test_negative_and_zero_scale(scale, d):
+    """The score scale is any finite float32: a negative one turns the peaked keys into the
+    least weighted, zero gives every visible key the same weight (the mean of their v)."""
+    rng = np.random.default_rng(11 + d)
+    pos = rng.integers(0, 3000, size=7)
+    case = workloads.decode_case("scale", 7, 4, 2, d, 300, 700, 2, pos, seed=d + 3, scale=scale,
+                                 peak_every=2)
+    _gate(case, f"decode scale {scale} d{d}")
+

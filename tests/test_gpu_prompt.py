@@ -357,3 +357,15 @@ def test_slot_stride_at_the_31_bit_limit(n, hq, hkv, d, p32):
     assert ok.all()
     assert np.array_equal(bits, gu.run_prompt(case))
 
+
+@pytest.mark.parametrize("scale", [-0.8, 0.0])
+@pytest.mark.parametrize("d,p32", [(256, True), (256, THREE), (256, False), (128, True)])
+def test_negative_and_zero_scale(scale, d, p32):
+    """Any finite float32 score scale: negative (the kernels carry its sign on q, exactly) or
+    zero (every visible key the same weight)."""
+    hi = 300 + np.arange(70)
+    hi[5:20] = 300 + 19
+    case = workloads.prompt_case("scale", 70, 4, 2, d, 300, 128, 512, seed=d + 5, hi=hi, p32=p32,
+                                 scale=scale, peak_every=2)
+    _gate(case, f"prompt scale {scale} d{d} p32={p32}")
+

@@ -193,3 +193,13 @@ def test_sparse_slot_stride_at_the_31_bit_limit():
     _, ok = gu.compare(bits, x, S, E_P[int(case.p32)], label)
     assert ok.all()
     assert np.array_equal(bits, gu.run_sparse(case))
+
+
+@pytest.mark.parametrize("scale", [-0.8, 0.0])
+@pytest.mark.parametrize("d", [256, 128])
+def test_negative_and_zero_scale(scale, d):
+    """Any finite float32 score scale through the block-sparse walk."""
+    case = workloads.sparse_prompt_case("scale", 24, 4, 2, d, 700, 4, seed=d + 9)
+    case.scale = scale
+    _gate(case, f"sparse scale {scale} d{d}")
+
