@@ -96,11 +96,13 @@ def test_decode_invariants():
     (36, 16, 16, 256, 1024, 1536, 2),    # one, d = 256
     (48, 8, 8, 128, 1024, 1536, 3),      # one, d = 128
     (40, 16, 8, 128, 1024, 1536, 3),     # two, d = 128
+    (32, 8, 8, 256, 1024, 1536, 32),     # whole rows (a stream a row), one query head a key head
 ])
 def test_large_grid_rows_match_rows_alone(rows, hq, hkv, d, win, ring, streams):
-    """Chunk grids of 1,024 workgroups or more (the kernel form with 8-key load units) pass the
-    gate, and a row alone (a small grid: the form with 16- or 32-key load units) gets the same
-    bits: the load unit never changes the arithmetic."""
+    """Chunk grids of 1,024 workgroups or more (the kernel form with 8-key load units), and
+    batches of rows in streams of their own (the whole-row kernel), pass the gate, and a row
+    alone (a small grid: the form with 16- or 32-key load units) gets the same bits: neither
+    the load unit nor the kernel form changes the arithmetic."""
     rng = np.random.default_rng(rows * 17 + hq + d)
     pos = rng.integers(0, 20001, size=rows)
     pos[:3] = [0, 255, 256]
