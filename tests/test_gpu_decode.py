@@ -195,6 +195,45 @@ def test_merge_reproduces_decode(rows, hq, hkv, d, win, ring, streams):
     assert np.array_equal(gu.host_bits(merged), gu.host_bits(out))
 
 
+def test_merge_of_foreign_partials():
+    """wa_merge on chunk partials made on the host — per 256-key chunk at absolute positions,
+    float64 sums rounded to fp32: m_c the chunk's largest score, l_c and o_c the sums of
+    exp(s - m_c) and exp(s - m_c) v — meets the oracle's gate and the literal rule: the merge
+    is checked apart from the kernel that usually feeds it."""
+    from sliding_window_gqa_amd import api
+    rows, hq, hkv, d, win, ring, streams = 9, 4, 2, 256, 700, 1024, 3
+    rng = np.random.default_rng(41)
+    pos = rng.integers(0, 5000, size=rows)
+    pos[:3] = [0, 255, 256]
+    case = workloads.decode_case("foreign partials", rows, hq, hkv, d, win, ring, streams, pos,
+                                 seed=43, peak_every=2)
+    C = api.lib().wa_decode_chunks(api.window(win, ring), api.INT32_MAX)
+    G = hq // hkv
+    bf = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    m = np.zeros((rows, hq, C), np.float32)
+    l_ = np.zeros((rows, hq, C), np.float32)
+    o = np.zeros((rows, hq, C, d), np.float32)
+    for r in range(rows):
+        p, t = int(case.pos[r]), int(case.stream[r])
+        lo = max(0, p - win + 1)
+        for h in range(hq):
+            qv = bf(case.q[r, h])
+            for k in range(p // 256 - lo // 256 + 1):
+                c = lo // 256 + k
+                js = np.arange(max(lo, 256 * c), min(p, 256 * c + 255) + 1)
+                s = float(np.float32(case.scale)) * (bf(case.k[t, js % ring, h // G]) @ qv)
+                mc = np.float32(s.max())
+                w = np.exp(s - float(mc))
+                m[r, h, k], l_[r, h, k] = mc, w.sum()
+                o[r, h, k] = w @ bf(case.v[t, js % ring, h // G])
+    dev = lambda a: torch.from_numpy(a).cuda()
+    merged = api.merge(dev(m), dev(l_), dev(o), gu.dev_i32(case.pos), win, ring)
+    torch.cuda.synchronize()
+    x, S, _ = gu.oracle_decode(case)
+    _, ok = gu.compare(gu.host_bits(merged), x, S, E_P, "merge of host partials")
+    assert ok.all()
+
+
 def test_decode_linear_cache_declared_longer():
     rows = 6
     pos = np.array([0, 100, 255, 256, 700, 999])
