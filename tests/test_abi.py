@@ -93,6 +93,26 @@ def test_decode_rejects_before_launch():
     assert _decode(w, ws=FAKE + 8) == WA_EWORKSPACE                  # workspace not 16-byte aligned
 
 
+WA_ESCRATCH = -6
+
+
+def test_noalloc_rejects_before_launch():
+    """wa_decode_noalloc refuses a call whose partials exceed its static scratch, and bad
+    shapes, before it touches a device."""
+    L = api.lib()
+
+    def call(rows, hq, hkv, d, w=api.window(1024, 1536)):
+        return L.wa_decode_noalloc(ctypes.byref(w), FAKE, 4096, 256, FAKE, FAKE, 0, 2048, 256, 1,
+                                   FAKE, FAKE, api.INT32_MAX, rows, hq, hkv, d, FAKE, 4096, 256,
+                                   None)
+    w = api.window(1024, 1536)
+    need = L.wa_decode_workspace(200, 16, 256, ctypes.byref(w), api.INT32_MAX)
+    assert need > 8 << 20
+    assert call(200, 16, 8, 256) == WA_ESCRATCH
+    assert call(0, 16, 8, 256) == WA_EARG
+    assert call(4, 16, 8, 64) == WA_EUNSUPPORTED
+
+
 def _prompt(w, p0=0, n=10, hq=4, hkv=2, d=256, ptr=FAKE, ws_bytes=1 << 30):
     L = api.lib()
     return L.wa_prompt(ctypes.byref(w), ptr, 1024, 256, ptr, ptr, 512, 256, p0, n, hq, hkv, d,
